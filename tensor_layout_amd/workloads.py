@@ -1,0 +1,82 @@
+"""The workloads the tests and the benchmark run, as plain shape/stride data.
+
+Each entry is a call in the library's form: element width in bytes, extents,
+source strides, destination strides (all in elements), element offsets
+(src, dst) and a contiguous batch count.  Seeds are 0x5EED0000 + 16 * case
+number + sub-case.  Nothing here computes an address.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Tuple
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    w: int
+    extents: Tuple[int, ...]
+    src_strides: Tuple[int, ...]
+    dst_strides: Tuple[int, ...]
+    offsets: Tuple[int, int] = (0, 0)
+    batch: int = 1
+    seed: int = 0
+    specials: bool = False   # force fp32 special encodings into the input
+
+    @property
+    def elements(self) -> int:
+        n = self.batch
+        for e in self.extents:
+            n *= e
+        return n
+
+    @property
+    def bytes_moved(self) -> int:
+        """Algorithmic bytes: every element read once and written once."""
+        return 2 * self.elements * self.w
+
+
+def _seed(case: int, sub: int = 0) -> int:
+    return 0x5EED0000 + 16 * case + sub
+
+
+# permute_layout page, "Demonstration program": two pipeline stages of a
+# (1, 4, 32) fp32 scale-factor block, (128,128,32,1) -> (128,128,1,4).
+SF_WORKED = Workload("sf_worked_example_2x1x4x32_f32", 4, (2, 1, 4, 32),
+                     (128, 128, 32, 1), (128, 128, 1, 4), seed=_seed(1))
+
+# 2**20 independent 4x32 fp32 tiles, contiguous batch (tile stride 128).
+SF_BATCHED = Workload("sf_transpose_2^20x4x32_f32", 4, (4, 32), (32, 1), (1, 4),
+                      batch=1 << 20, seed=_seed(2), specials=True)
+
+# 65536 tiles of 128x64 fp16: row-major (64,1) -> column-major (1,128).
+TILE_128x64 = Workload("tile_65536x128x64_f16_rowmajor_to_colmajor", 2, (128, 64), (64, 1),
+                       (1, 128), batch=65536, seed=_seed(3))
+
+
+def mixed_width(w: int) -> Workload:
+    """(64,128,32,32) permuted by axis order (0,2,3,1); destination is the
+    row-major layout of the permuted shape (64,32,32,128)."""
+    sub = {1: 0, 2: 1, 4: 2, 8: 3}[w]
+    return Workload(f"axes0231_64x128x32x32_w{w}", w, (64, 128, 32, 32),
+                    (131072, 1024, 32, 1), (131072, 1, 4096, 128), seed=_seed(4, sub))
+
+
+BF16_16K = Workload("transpose_16384x16384_bf16", 2, (16384, 16384), (16384, 1), (1, 16384),
+                    seed=_seed(5, 0))
+W16_4K = Workload("transpose_4096x4096_16B", 16, (4096, 4096), (4096, 1), (1, 4096),
+                  seed=_seed(5, 1))
+
+ALL = [SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)] + [BF16_16K, W16_4K]
+
+
+def scaled(wl: Workload, batch: int = None, extents=None) -> Workload:
+    """The same layouts on a smaller batch or extents (for CPU-sized parity cases)."""
+    from dataclasses import replace
+    kw = {}
+    if batch is not None:
+        kw["batch"] = batch
+    if extents is not None:
+        kw["extents"] = tuple(extents)
+    return replace(wl, **kw)
