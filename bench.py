@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of permute_layout on one MI355X.
+
+Default workload: the batched scale-factor transpose, 2^20 independent 4x32
+fp32 tiles (source strides (32, 1), destination (1, 4), tile stride 128
+elements), 512 MiB in and 512 MiB out.  A step is one call of tpl_permute on
+the whole batch, with the inputs already resident in HBM.  Source/destination
+pairs rotate so that no step finds its data in the 256 MB Infinity Cache.
+
+Prints ONE JSON line: whole-job GB/s (bytes read + written per second), the
+roofline block of the dominant kernel (HIP-event time per launch on the
+launch stream), the oracle's CPU throughput on the host, and the measured HBM
+traffic from the committed rocprofv3 counter summary when it matches the
+current kernel source.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "permute_layout GB/s (rd+wr) & % of HBM peak, batched 4x32 fp32 SF transpose"
+PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+ROTATE_BYTES = 2 << 30      # src+dst bytes cycled through per rotation
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "tensor_layout_amd", "csrc", f)
+                  for f in ("kernels.hip", "common.hpp", "planner.cpp", "planner.hpp")]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(name: str):
+    """Counter-measured HBM bytes per launch, or None when absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_hash():
+        return None
+    rec = t.get("workloads", {}).get(name)
+    if not rec:
+        return None
+    return int(rec["fetch_bytes"] + rec["write_bytes"])
+
+
+def dtype_name(w: int, specials: bool) -> str:
+    return {1: "u8", 2: "u16", 4: "u32", 8: "u64", 16: "u128"}[w]
+
+
+def make_input(wl):
+    import numpy as np
+    from tensor_layout_amd import synth
+    x = synth.random_bytes(wl.seed, wl.elements * wl.w).copy()
+    if wl.specials and wl.w == 4:
+        synth.inject_f32_specials(x.view(np.uint32), wl.seed ^ 0x5EC1A1)
+    return x
+
+
+def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
+    """The oracle as it stands, single-threaded, on the full workload."""
+    import numpy as np
+    import oracle
+    y = np.empty(wl.elements * wl.w, dtype=np.uint8)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or runs >= max_runs:
+            break
+    return {
+        "value": round(wl.bytes_moved * runs / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the full workload ({wl.elements} elements) permuted {runs} times by the "
+                  f"single-threaded C oracle in {el:.1f} s",
+    }, y
+
+
+def bench_one(wl, steps, warmup, do_cpu, do_verify):
+    import numpy as np
+    import torch
+    from tensor_layout_amd import tpl
+
+    dev = torch.device("cuda:0")
+    x = make_input(wl)
+    nbytes = wl.elements * wl.w
+    pairs = max(2, min(128, math.ceil(ROTATE_BYTES / (2 * nbytes))))
+    srcs = [torch.from_numpy(x).to(dev)]
+    for _ in range(pairs - 1):
+        srcs.append(srcs[0].clone())
+    dsts = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(pairs)]
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    args = (wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch, sp)
+    plan = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
+
+    def launch(i):
+        st = tpl.tpl_permute(srcs[i % pairs].data_ptr(), dsts[i % pairs].data_ptr(), *args)
+        if st != tpl.TPL_OK:
+            raise tpl.TplError(st, tpl.tpl_last_error())
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_ms = sum(kernel_ms) / len(kernel_ms)
+    elapsed = t1 - t0
+    value = wl.bytes_moved * steps / elapsed / 1e9
+    achieved = wl.bytes_moved / (avg_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC if wl.name.startswith("sf_transpose") else f"permute_layout GB/s (rd+wr), {wl.name}",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(elapsed * 1e3 / steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name(wl.w, wl.specials),
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "elements": wl.elements,
+            "element_bytes": wl.w,
+            "bytes_per_step": wl.bytes_moved,
+            "kernel": plan.kernel,
+            "tile": list(plan.tile),
+            "k": plan.k, "shift": plan.shift, "mask": plan.mask,
+            "buffer_pairs": pairs,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4),
+            "traffic": traffic_for(wl.name),
+            "kernel_ms_avg": round(avg_ms, 5),
+            "kernel_ms_min": round(min(kernel_ms), 5),
+        },
+    }
+    ref = None
+    if do_cpu:
+        out["cpu_baseline"], ref = cpu_baseline(wl, x)
+    if do_verify:
+        import oracle
+        if ref is None:
+            ref = np.empty(nbytes, dtype=np.uint8)
+            oracle.permute(x, ref, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
+        last = (warmup + steps - 1) % pairs
+        got = dsts[last].cpu().numpy()
+        out["bitexact"] = bool(np.array_equal(got, ref))
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sf_transpose_2^20x4x32_f32")
+    ap.add_argument("--all", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-verify", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from tensor_layout_amd import tpl, workloads
+    tpl.load()
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    by_name = {w.name: w for w in workloads.ALL}
+    if a.all:
+        for wl in workloads.ALL:
+            print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify)), flush=True)
+        return
+    wl = by_name[a.workload]
+    print(json.dumps(bench_one(wl, a.steps, a.warmup, not a.no_cpu, not a.no_verify)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

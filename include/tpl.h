@@ -1,0 +1,132 @@
+/*
+ * tpl.h -- C ABI of the permute_layout library for MI355X (gfx950).
+ *
+ * The operation (permute_layout page, intro and "Algorithm"; address rule from
+ * the "Buffers and memory" page, "Declaring buffers"): every element of a
+ * tensor held under a source shape:stride layout is copied, bit for bit, to
+ * the place the destination layout gives the same logical coordinate.
+ *
+ * For every batch index b < batch and every coordinate c of `extents`:
+ *
+ *   dst[off_d + b*span_d + sum_i c_i*dst_strides[i]] :=
+ *       src[off_s + b*span_s + sum_i c_i*src_strides[i]]
+ *
+ * with strides and offsets counted in elements of `dtype_bytes` bytes, and
+ * span_x = 1 + sum_i (extents[i]-1)*x_strides[i] (the side's cosize: batch
+ * items follow each other with no gap).  A batch with another spacing is one
+ * more leading mode with batch = 1.  The bytes move verbatim; nothing is
+ * interpreted as a number.
+ *
+ * Operand rules (permute_layout page, "What it accepts"): one element width
+ * for both sides, equal extents (a single `extents` array here), width in
+ * {1, 2, 4, 8, 16}, plain shape:stride layouts, and a conflict-free XOR
+ * swizzle must exist for the staged exchange, else the call declines.
+ */
+#ifndef TPL_H
+#define TPL_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every check runs before anything is enqueued: on a non-OK
+ * return nothing was launched and dst is untouched. */
+typedef enum {
+    TPL_OK = 0,
+    TPL_E_ARG = 1,          /* null pointer, rank outside 1..8, negative extent or batch */
+    TPL_E_DTYPE_WIDTH = 2,  /* dtype_bytes not in {1, 2, 4, 8, 16} */
+    TPL_E_DTYPE = 3,        /* element types differ (raised by the Python binding) */
+    TPL_E_EXTENT = 4,       /* extents differ (raised by the Python binding) */
+    TPL_E_LAYOUT = 5,       /* layout cannot be canonicalised: negative stride or offset,
+                               destination not provably one-to-one, offsets overflow */
+    TPL_E_NO_K = 6,         /* no XOR swizzle makes both staged phases conflict-free */
+    TPL_E_ALIAS = 7,        /* src and dst overlap other than unit-for-unit in place */
+    TPL_E_HIP = 8           /* the HIP runtime refused the launch; see tpl_last_error() */
+} tpl_status;
+
+/* Bank geometry for tpl_plan. */
+enum {
+    TPL_GEOM_GFX950 = 0,   /* the kernels this library launches on gfx950 (64-lane waves,
+                              LDS banks as measured on MI355X) */
+    TPL_GEOM_PAGES32 = 1   /* the pages' warp program: 32 lanes, 32 banks of 4 bytes */
+};
+
+/* Kernel families a GFX950 plan can pick. */
+enum {
+    TPL_KERNEL_NONE = 0,   /* nothing to do (empty tensor) or a PAGES32 plan */
+    TPL_KERNEL_GATHER = 1, /* element-wise gather/scatter, any layout */
+    TPL_KERNEL_QUAD = 2,   /* 4x4 fp32 blocks transposed in registers by lane quads (DPP) */
+    TPL_KERNEL_LDS = 3,    /* tiled 2-D transpose staged through LDS with XOR-ordered phases */
+    TPL_KERNEL_REG16 = 4,  /* 16-byte elements: 8x8 element blocks, pure lane remap */
+    TPL_KERNEL_COPY = 5    /* both sides contiguous along one mode: vector copy of runs */
+};
+
+#define TPL_MAX_RANK 8
+#define TPL_MAX_SHARD 10
+
+typedef struct {
+    int32_t status;                 /* tpl_status of the planning */
+    int32_t rank;                   /* modes in the shard (batch folded in as a mode) */
+    int64_t extent[TPL_MAX_SHARD];  /* shard extents, outermost first */
+    int64_t src_str[TPL_MAX_SHARD]; /* shard source strides (elements) */
+    int64_t dst_str[TPL_MAX_SHARD]; /* shard destination strides (elements) */
+    int64_t P;                      /* elements staged per lane per phase */
+    int32_t k, shift, mask;         /* XOR swizzle j = r ^ ((lane >> shift) & mask) of the
+                                       exchange's read phase (PAGES32: of both phases) */
+    int32_t k_w, shift_w, mask_w;   /* GFX950 LDS kernel: XOR of the LDS write phase */
+    int32_t kernel;                 /* TPL_KERNEL_* (GFX950 only) */
+    int32_t tile[2];                /* tile extents (b, a) in elements, LDS/QUAD kernels */
+    int32_t lds_pitch;              /* LDS row pitch in bytes, LDS kernel */
+    int64_t grid, block;            /* launch shape of the main kernel */
+} tpl_plan_info;
+
+/*
+ * Enqueue the permutation on `stream` and return without waiting.
+ *
+ * src, dst      device pointers (caller-owned; the library never allocates).
+ * dtype_bytes   element width shared by both sides.
+ * rank          number of modes, 1..8; extents/src_strides/dst_strides have
+ *               `rank` entries each (host arrays, borrowed for the call).
+ * elem_offsets  host array {src offset, dst offset} in elements (may be NULL
+ *               for {0, 0}).
+ * batch         number of contiguous batch items (>= 0; 0 does nothing).
+ * stream        HIP stream (NULL = the null stream).
+ *
+ * Source and destination may be the same memory only when every work unit's
+ * source footprint equals its destination footprint (e.g. an in-place
+ * transpose of each batch item); any other overlap returns TPL_E_ALIAS.
+ * Returns a tpl_status; thread-safe.
+ */
+int tpl_permute(const void *src, void *dst, int dtype_bytes, int rank,
+                const int64_t *extents, const int64_t *src_strides,
+                const int64_t *dst_strides, const int64_t *elem_offsets,
+                int64_t batch, hipStream_t stream);
+
+/*
+ * Host-only planning, no device needed.  With TPL_GEOM_PAGES32 it runs the
+ * pages' method on one warp region: shard, P = elements / 32, and the
+ * smallest k whose XOR swizzle makes the read and the write phase
+ * bank-conflict-free (declines with TPL_E_NO_K otherwise).  With
+ * TPL_GEOM_GFX950 it returns the plan tpl_permute would launch (assuming
+ * 256-byte aligned base pointers).  `out` is filled on every return.
+ * elem_offsets may be NULL.
+ */
+int tpl_plan(int dtype_bytes, int rank, const int64_t *extents,
+             const int64_t *src_strides, const int64_t *dst_strides,
+             const int64_t *elem_offsets, int64_t batch, int geometry,
+             tpl_plan_info *out);
+
+/* Static text of a status code. */
+const char *tpl_status_string(int status);
+
+/* Reason text of this thread's last non-OK return (empty string if none). */
+const char *tpl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPL_H */

@@ -1,0 +1,195 @@
+// common.hpp -- types shared by the host planner and the gfx950 kernels.
+//
+// Everything here is plain data plus small __host__ __device__ index helpers.
+// The lane -> LDS address maps of the tiled kernel live here so that the
+// planner's bank simulation runs exactly the addresses the kernel issues.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#define TPL_HD __host__ __device__ __forceinline__
+#else
+#define TPL_HD inline
+#endif
+
+namespace tpl {
+
+constexpr int kMaxShard = 10;   // shard modes (8 user modes + batch + slack)
+constexpr int kMaxBatch = 8;    // modes a kernel decomposes as "batch"
+constexpr int kWave = 64;       // gfx950 wavefront
+
+// Division by an invariant 31-bit integer with a multiply and a shift
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", 1994, round-up variant): for 0 <= n < 2^31 and
+// 1 <= d < 2^31, n / d = (umulhi(n, m) + n) >> s with s = ceil(log2 d) and
+// m = floor(2^32 * (2^s - d) / d) + 1.
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.s = s;
+    f.m = (uint32_t)((((1ull << s) - d) << 32) / d + 1);
+    return f;
+}
+
+TPL_HD uint32_t fdiv(uint32_t n, const FastDiv& f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t hi = __umulhi(n, f.m);
+#else
+    uint32_t hi = (uint32_t)(((uint64_t)n * f.m) >> 32);
+#endif
+    return (hi + n) >> f.s;
+}
+
+// Row-major decomposition of a linear index over up to kMaxBatch modes,
+// returning the source and destination element offsets of that index.
+struct Modes {
+    int n;
+    FastDiv div[kMaxBatch];   // extents, innermost last
+    int64_t ext[kMaxBatch];
+    int64_t ss[kMaxBatch];    // source strides (elements)
+    int64_t ds[kMaxBatch];    // destination strides (elements)
+};
+
+template <bool BIG>
+TPL_HD void modes_offsets(const Modes& m, int64_t idx, int64_t& so, int64_t& d_o) {
+    so = 0;
+    d_o = 0;
+    for (int i = m.n - 1; i >= 0; --i) {
+        int64_t q, r;
+        if (BIG) {
+            q = idx / m.ext[i];
+            r = idx - q * m.ext[i];
+        } else {
+            uint32_t qq = fdiv((uint32_t)idx, m.div[i]);
+            r = (int64_t)((uint32_t)idx - qq * m.div[i].d);
+            q = qq;
+        }
+        so += r * m.ss[i];
+        d_o += r * m.ds[i];
+        idx = q;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel argument blocks (passed by value).
+
+struct GatherArgs {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t total;   // elements
+    Modes modes;     // the whole shard
+    int unit;        // bytes moved per access (divides the element width)
+    int w;
+};
+
+struct CopyArgs {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t nchunks;     // 16-byte chunks overall
+    FastDiv div_cpr;     // chunks per run
+    int64_t cpr;
+    Modes rows;          // the modes outside the contiguous run
+    int w;
+};
+
+struct QuadArgs {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t nquads;      // 4x4 blocks overall
+    FastDiv div_qpr;     // 4x4 blocks per batch item (e_a / 4)
+    int64_t qpr;
+    int64_t s_b;         // source stride of the 4-row mode (elements)
+    int64_t d_a;         // destination stride of the contiguous-source mode (elements)
+    Modes batch;
+};
+
+struct LdsArgs {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t e_b, e_a;    // b: destination-contiguous mode, a: source-contiguous mode
+    int64_t s_b, d_a;    // the two non-unit strides (elements)
+    int64_t ntiles;
+    int64_t ntb, nta;
+    FastDiv div_nta, div_ntb;
+    Modes batch;
+    int32_t pitch;       // LDS row pitch, bytes
+    int32_t shift_r, mask_r, shift_w, mask_w;
+};
+
+struct Reg16Args {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t e_b, e_a, s_b, d_a;
+    int64_t nblocks;     // 8x8 element blocks overall
+    int64_t nbb, nba;
+    FastDiv div_nba, div_nbb;
+    Modes batch;
+};
+
+// ---------------------------------------------------------------------------
+// Tiled LDS kernel geometry: one workgroup moves one TB x TA tile
+// (TB along the destination-contiguous mode b, TA along the
+// source-contiguous mode a).  NT = tile_bytes / 64 threads, each thread
+// loading four 16-byte chunks.
+
+struct LdsShape {
+    int w, tb, ta;
+    constexpr TPL_HD int row_bytes() const { return ta * w; }            // one source row in the tile
+    constexpr TPL_HD int chunks_per_row() const { return ta * w / 16; }
+    constexpr TPL_HD int tile_bytes() const { return tb * ta * w; }
+    constexpr TPL_HD int threads() const { return tile_bytes() / 64; }
+    constexpr TPL_HD int g() const { return w >= 4 ? 1 : 4 / w; }         // elements per dword
+    constexpr TPL_HD int read_bytes() const { return w >= 8 ? 8 : 4; }    // LDS read width
+    constexpr TPL_HD int reads_per_group() const { return w >= 8 ? 2 : 4 * g(); }  // P of the read phase
+    constexpr TPL_HD int nq() const { return tb * w / 16; }              // 16-byte chunks per destination row
+    constexpr TPL_HD int ql() const { return nq() < 8 ? nq() : 8; }      // chunks along b in neighbouring lanes
+    constexpr TPL_HD int cols() const { return w >= 8 ? ta : ta * w / 4; } // read columns (dwords, or 8-byte elements)
+    constexpr TPL_HD int groups() const { return cols() * nq(); }
+    constexpr TPL_HD int groups_per_thread() const { return groups() / threads(); }
+};
+
+// Write phase: thread t, chunk slot k (0..3), piece step r of the chunk.
+// Returns the LDS byte address; `piece` receives the piece index written.
+TPL_HD int lds_write_addr(const LdsShape& sh, int pitch, int ww, int t, int k, int r,
+                          int shift_w, int mask_w, int* piece) {
+    int cid = t + k * sh.threads();
+    int row = cid / sh.chunks_per_row();
+    int c = cid % sh.chunks_per_row();
+    int lane = t & (kWave - 1);
+    int h = r ^ ((lane >> shift_w) & mask_w);
+    if (piece) *piece = h;
+    return row * pitch + c * 16 + h * ww;
+}
+
+// Read phase: thread t, group slot k2, unrolled read step r.
+// Group gid -> (column col, chunk q): lanes run along q first (QL of them),
+// then along col, then over the rest of q.
+TPL_HD void lds_group(const LdsShape& sh, int t, int k2, int* col, int* q) {
+    int gid = t + k2 * sh.threads();
+    int ql = sh.ql();
+    int seg = gid % ql;
+    int rest = gid / ql;
+    *col = rest % sh.cols();
+    *q = (rest / sh.cols()) * ql + seg;
+}
+
+TPL_HD int lds_read_addr(const LdsShape& sh, int pitch, int t, int k2, int r,
+                         int shift_r, int mask_r, int* row_step) {
+    int col, q;
+    lds_group(sh, t, k2, &col, &q);
+    int lane = t & (kWave - 1);
+    int j = r ^ ((lane >> shift_r) & mask_r);
+    if (row_step) *row_step = j;
+    int b0 = q * sh.reads_per_group();
+    return (b0 + j) * pitch + col * sh.read_bytes();
+}
+
+}  // namespace tpl

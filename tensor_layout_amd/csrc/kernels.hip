@@ -1,0 +1,647 @@
+// kernels.hip -- gfx950 kernels of permute_layout and the C entry points.
+//
+// permute_layout page, "Algorithm" step 3: each lane reads its elements
+// through the source layout into registers, the lanes synchronise, and the
+// registers are written back through the destination layout.  On gfx950 the
+// reads and writes go to HBM, so both sides are 16-byte vector accesses that
+// cover whole 128-byte lines, and the element exchange between them happens
+// in registers (lane quads, DPP) or through LDS with XOR-ordered phases.
+// Data moves as integers only; no floating-point instruction touches it.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "common.hpp"
+#include "planner.hpp"
+
+namespace tpl {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kQuadUnroll = 2;
+constexpr int64_t kMaxThreads = (int64_t)1 << 31;   // grid * block kept below 2^32
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(uint8_t* p, u32x4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+template <bool BIG>
+__device__ __forceinline__ void split(int64_t idx, int64_t n, const FastDiv& f, int64_t& q, int64_t& r) {
+    if (BIG) {
+        q = idx / n;
+        r = idx - q * n;
+    } else {
+        uint32_t qq = fdiv((uint32_t)idx, f);
+        q = qq;
+        r = (int64_t)((uint32_t)idx - qq * f.d);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Gather/scatter: one element per thread per iteration, any layout.
+
+template <typename T>
+struct Unit;
+template <> struct Unit<uint8_t> { static constexpr int bytes = 1; };
+template <> struct Unit<uint16_t> { static constexpr int bytes = 2; };
+template <> struct Unit<uint32_t> { static constexpr int bytes = 4; };
+template <> struct Unit<uint64_t> { static constexpr int bytes = 8; };
+template <> struct Unit<u32x4> { static constexpr int bytes = 16; };
+
+template <typename T, bool BIG>
+__global__ void __launch_bounds__(256) k_gather(GatherArgs a) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int nu = a.w / Unit<T>::bytes;
+    for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < a.total; n += stride) {
+        int64_t so, d_o;
+        modes_offsets<BIG>(a.modes, n, so, d_o);
+        const T* s = reinterpret_cast<const T*>(a.src + so * a.w);
+        T* d = reinterpret_cast<T*>(a.dst + d_o * a.w);
+        for (int u = 0; u < nu; ++u) d[u] = s[u];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Copy: both sides contiguous along one mode; 16-byte chunks of the runs.
+
+template <bool BIG>
+__global__ void __launch_bounds__(256) k_copy(CopyArgs a) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < a.nchunks; id += stride) {
+        int64_t row, c;
+        split<BIG>(id, a.cpr, a.div_cpr, row, c);
+        int64_t so, d_o;
+        modes_offsets<BIG>(a.rows, row, so, d_o);
+        st16(a.dst + d_o * a.w + c * 16, ld16(a.src + so * a.w + c * 16));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Quad kernel: fp32 tiles whose destination-contiguous mode has extent 4.
+// A lane quad loads a 4x4 block (lane i: row i, four consecutive columns),
+// transposes it across the quad with two DPP exchange stages, and lane i
+// stores column i (four rows, 16 contiguous bytes).  A wave moves 16 blocks
+// per instruction; for the 4x32 scale-factor tile that is two whole tiles,
+// every 128-byte line of which is read and written by one instruction.
+
+__device__ __forceinline__ uint32_t quad_swap1(uint32_t x) {   // lane i reads lane i^1
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t quad_swap2(uint32_t x) {   // lane i reads lane i^2
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 v, int i) {
+    // Stage 1: lanes i, i^1 swap the entries whose column parity differs
+    // from their row parity.  Stage 2: the same with bit 1 and lanes i^2.
+    const bool odd = i & 1, hi = i & 2;
+    uint32_t x0 = v.x, x1 = v.y, x2 = v.z, x3 = v.w;
+    uint32_t u0 = quad_swap1(odd ? x0 : x1);
+    uint32_t u1 = quad_swap1(odd ? x2 : x3);
+    uint32_t a0 = odd ? u0 : x0, a1 = odd ? x1 : u0;
+    uint32_t a2 = odd ? u1 : x2, a3 = odd ? x3 : u1;
+    uint32_t u2 = quad_swap2(hi ? a0 : a2);
+    uint32_t u3 = quad_swap2(hi ? a1 : a3);
+    u32x4 y;
+    y.x = hi ? u2 : a0;
+    y.y = hi ? u3 : a1;
+    y.z = hi ? a2 : u2;
+    y.w = hi ? a3 : u3;
+    return y;
+}
+
+template <int U, bool BIG>
+__global__ void __launch_bounds__(256) k_quad(QuadArgs a) {
+    const int i = threadIdx.x & 3;
+    const int qi = threadIdx.x >> 2;   // 64 quads per workgroup step
+    for (int64_t base = (int64_t)blockIdx.x * U * 64; base < a.nquads; base += (int64_t)gridDim.x * U * 64) {
+        u32x4 v[U];
+        int64_t dofs[U];
+        bool act[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t Q = base + u * 64 + qi;
+            act[u] = Q < a.nquads;
+            v[u] = u32x4{0, 0, 0, 0};
+            dofs[u] = 0;
+            if (act[u]) {
+                int64_t item, qa;
+                split<BIG>(Q, a.qpr, a.div_qpr, item, qa);
+                int64_t so, d_o;
+                modes_offsets<BIG>(a.batch, item, so, d_o);
+                v[u] = ld16(a.src + (so + i * a.s_b + 4 * qa) * 4);
+                dofs[u] = (d_o + (4 * qa + i) * a.d_a) * 4;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            u32x4 y = quad_transpose(v[u], i);
+            if (act[u]) st16(a.dst + dofs[u], y);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// LDS kernel: one workgroup moves a TB x TA tile (TB along the destination-
+// contiguous mode b, TA along the source-contiguous mode a).
+//
+// Phase 1: every thread loads four 16-byte chunks of source rows and writes
+// them to LDS (row pitch chosen by the planner) in 16/WW pieces, the piece
+// order XOR-rotated per lane: piece = r ^ ((lane >> shift_w) & mask_w).
+// Barrier.  Phase 2: every thread gathers, for one column of the tile and
+// one 16-byte destination chunk, the rows b0 .. b0+P-1 of that column, in the
+// order j = r ^ ((lane >> shift_r) & mask_r), restores row order in
+// registers, packs sub-dword elements into destination-order dwords and
+// stores 16 bytes.  Both XORs are the planner's smallest conflict-free k for
+// the measured gfx950 LDS banks.
+
+template <int N>
+__device__ __forceinline__ void unrotate(uint32_t (&d)[N], int key) {
+    // d[r] holds row r ^ key; afterwards d[m] holds row m.
+#pragma unroll
+    for (int bi = 0; (1 << bi) < N; ++bi) {
+        const bool sw = (key >> bi) & 1;
+#pragma unroll
+        for (int x = 0; x < N; ++x) {
+            if (x & (1 << bi)) continue;
+            uint32_t p0 = d[x], p1 = d[x | (1 << bi)];
+            d[x] = sw ? p1 : p0;
+            d[x | (1 << bi)] = sw ? p0 : p1;
+        }
+    }
+}
+
+template <int W, int TB, int TA, int WW, bool BIG>
+__global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
+    constexpr LdsShape SH{W, TB, TA};
+    constexpr int NT = TB * TA * W / 64;
+    constexpr int CPR = TA * W / 16;
+    constexpr int G = (W >= 4) ? 1 : 4 / W;
+    constexpr int R = (W >= 8) ? 2 : 4 * G;          // reads per group
+    constexpr int GPT = SH.groups() / NT;             // groups per thread
+    constexpr int NP = 16 / WW;                       // pieces per chunk
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int key_w = (lane >> a.shift_w) & a.mask_w;
+    const int key_r = (lane >> a.shift_r) & a.mask_r;
+    const int pitch = a.pitch;
+
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        int64_t rest, tai, item, tbi;
+        split<BIG>(tile, a.nta, a.div_nta, rest, tai);
+        split<BIG>(rest, a.ntb, a.div_ntb, item, tbi);
+        int64_t so, d_o;
+        modes_offsets<BIG>(a.batch, item, so, d_o);
+        const int64_t b0 = tbi * TB, a0 = tai * TA;
+
+        if (b0 + TB > a.e_b || a0 + TA > a.e_a) {
+            // Ragged edge tile: element by element (never used in place).
+            const int nb = (int)(a.e_b - b0 < TB ? a.e_b - b0 : TB), na = (int)(a.e_a - a0 < TA ? a.e_a - a0 : TA);
+            for (int idx = t; idx < TB * TA; idx += NT) {
+                const int bb = idx / TA, aa = idx % TA;
+                if (bb >= nb || aa >= na) continue;
+                const uint8_t* s = a.src + (so + (b0 + bb) * a.s_b + a0 + aa) * W;
+                uint8_t* d = a.dst + (d_o + (a0 + aa) * a.d_a + b0 + bb) * W;
+                if (W == 1) *d = *s;
+                else if (W == 2) *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
+                else if (W == 4) *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
+                else *reinterpret_cast<uint64_t*>(d) = *reinterpret_cast<const uint64_t*>(s);
+            }
+            continue;   // uniform across the workgroup
+        }
+
+        const uint8_t* st = a.src + (so + b0 * a.s_b + a0) * W;
+        uint8_t* dt = a.dst + (d_o + a0 * a.d_a + b0) * W;
+        const int64_t srow = a.s_b * W;
+
+        // Phase 1: HBM -> registers -> LDS.
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int cid = t + k * NT;
+            v[k] = ld16(st + (cid / CPR) * srow + (cid % CPR) * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int cid = t + k * NT;
+            uint8_t* row = lds + (cid / CPR) * pitch + (cid % CPR) * 16;
+            if (NP == 1) {
+                *reinterpret_cast<u32x4*>(row) = v[k];
+            } else if (NP == 2) {
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int h = r ^ key_w;
+                    u32x2 p = h ? u32x2{v[k].z, v[k].w} : u32x2{v[k].x, v[k].y};
+                    *reinterpret_cast<u32x2*>(row + h * 8) = p;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int h = r ^ key_w;
+                    uint32_t p = h == 0 ? v[k].x : h == 1 ? v[k].y : h == 2 ? v[k].z : v[k].w;
+                    *reinterpret_cast<uint32_t*>(row + h * 4) = p;
+                }
+            }
+        }
+        __syncthreads();
+
+        // Phase 2: LDS -> registers -> HBM.
+#pragma unroll
+        for (int k2 = 0; k2 < GPT; ++k2) {
+            int col, q;
+            lds_group(SH, t, k2, &col, &q);
+            const uint8_t* base = lds + (q * R) * pitch + col * (W >= 8 ? 8 : 4);
+            if (W >= 8) {
+                uint32_t lo[2], hi[2];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int j = r ^ key_r;
+                    u32x2 x = *reinterpret_cast<const u32x2*>(base + j * pitch);
+                    lo[r] = x.x;
+                    hi[r] = x.y;
+                }
+                unrotate<2>(lo, key_r);
+                unrotate<2>(hi, key_r);
+                st16(dt + (int64_t)col * a.d_a * W + q * 16, u32x4{lo[0], hi[0], lo[1], hi[1]});
+            } else {
+                uint32_t d[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int j = r ^ key_r;
+                    d[r] = *reinterpret_cast<const uint32_t*>(base + j * pitch);
+                }
+                unrotate<R>(d, key_r);
+                if (W == 4) {
+                    st16(dt + (int64_t)col * a.d_a * 4 + q * 16, u32x4{d[0], d[1], d[2], d[3]});
+                } else if (W == 2) {
+                    // d[m] = (b0+m, a=2col) | (b0+m, a=2col+1) << 16
+                    u32x4 o0, o1;
+                    uint32_t* p0 = reinterpret_cast<uint32_t*>(&o0);
+                    uint32_t* p1 = reinterpret_cast<uint32_t*>(&o1);
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const uint32_t x = d[2 * kk], y = d[2 * kk + 1];
+                        p0[kk] = (x & 0xffffu) | (y << 16);
+                        p1[kk] = (x >> 16) | (y & 0xffff0000u);
+                    }
+                    uint8_t* out = dt + (int64_t)(2 * col) * a.d_a * 2 + q * 16;
+                    st16(out, o0);
+                    st16(out + a.d_a * 2, o1);
+                } else {
+                    // W == 1: d[m] holds bytes (b0+m, a=4col+t), t = 0..3.
+                    u32x4 o[4];
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        uint32_t* p = reinterpret_cast<uint32_t*>(&o[tt]);
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) {
+                            const int sh = 8 * tt;
+                            p[kk] = ((d[4 * kk] >> sh) & 0xffu) | (((d[4 * kk + 1] >> sh) & 0xffu) << 8) |
+                                    (((d[4 * kk + 2] >> sh) & 0xffu) << 16) | (((d[4 * kk + 3] >> sh) & 0xffu) << 24);
+                        }
+                    }
+                    uint8_t* out = dt + (int64_t)(4 * col) * a.d_a + q * 16;
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) st16(out + tt * a.d_a, o[tt]);
+                }
+            }
+        }
+        __syncthreads();   // LDS is reused by the next tile of this workgroup
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 16-byte elements: a wave takes an 8x8 element block; lane (i, j) loads
+// source row b0+i, element a0+j (eight lanes per 128-byte source line) and
+// stores it at destination row a0+j, element b0+i (eight lanes per 128-byte
+// destination line).  An element is one dwordx4, so no exchange is needed.
+
+template <bool BIG>
+__global__ void __launch_bounds__(256) k_reg16(Reg16Args a) {
+    const int lane = threadIdx.x & 63;
+    const int i = lane >> 3, j = lane & 7;
+    for (int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); blk < a.nblocks;
+         blk += (int64_t)gridDim.x * 4) {
+        int64_t rest, tai, item, tbi;
+        split<BIG>(blk, a.nba, a.div_nba, rest, tai);
+        split<BIG>(rest, a.nbb, a.div_nbb, item, tbi);
+        int64_t so, d_o;
+        modes_offsets<BIG>(a.batch, item, so, d_o);
+        const int64_t bb = tbi * 8 + i, aa = tai * 8 + j;
+        if (bb < a.e_b && aa < a.e_a)
+            st16(a.dst + (d_o + aa * a.d_a + bb) * 16, ld16(a.src + (so + bb * a.s_b + aa) * 16));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch.
+
+static int64_t cap_grid(int64_t grid, int64_t block) {
+    int64_t lim = kMaxThreads / block;
+    return grid < lim ? (grid < 1 ? 1 : grid) : lim;
+}
+
+template <bool BIG>
+static hipError_t launch_lds(const Plan& p, hipStream_t st) {
+    dim3 grid((unsigned)cap_grid(p.grid, p.block)), block((unsigned)p.block);
+    const LdsArgs& a = p.lds;
+    const int w = p.w, tb = p.tile_b, ta = p.tile_a, ww = p.ww;
+#define TPL_LDS_CASE(W_, TB_, TA_, WW_)                                                         \
+    if (w == W_ && tb == TB_ && ta == TA_ && ww == WW_) {                                        \
+        hipLaunchKernelGGL((k_lds<W_, TB_, TA_, WW_, BIG>), grid, block, p.lds_bytes, st, a);   \
+        return hipGetLastError();                                                                \
+    }
+#define TPL_LDS_SHAPE(W_, TB_, TA_) TPL_LDS_CASE(W_, TB_, TA_, 16) TPL_LDS_CASE(W_, TB_, TA_, 8) TPL_LDS_CASE(W_, TB_, TA_, 4)
+    TPL_LDS_SHAPE(1, 128, 128)
+    TPL_LDS_SHAPE(1, 64, 128)
+    TPL_LDS_SHAPE(2, 128, 64)
+    TPL_LDS_SHAPE(2, 32, 64)
+    TPL_LDS_SHAPE(4, 64, 64)
+    TPL_LDS_SHAPE(4, 32, 32)
+    TPL_LDS_SHAPE(8, 32, 64)
+    TPL_LDS_SHAPE(8, 16, 32)
+#undef TPL_LDS_SHAPE
+#undef TPL_LDS_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+template <bool BIG>
+static hipError_t launch_big(const Plan& p, const uint8_t* src, uint8_t* dst, hipStream_t st) {
+    switch (p.kernel) {
+    case TPL_KERNEL_GATHER: {
+        GatherArgs a = p.gather;
+        a.src = src;
+        a.dst = dst;
+        dim3 grid((unsigned)cap_grid(p.grid, 256)), block(256);
+        switch (a.unit) {
+        case 1: hipLaunchKernelGGL((k_gather<uint8_t, BIG>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((k_gather<uint16_t, BIG>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((k_gather<uint32_t, BIG>), grid, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((k_gather<uint64_t, BIG>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((k_gather<u32x4, BIG>), grid, block, 0, st, a); break;
+        }
+        return hipGetLastError();
+    }
+    case TPL_KERNEL_COPY: {
+        CopyArgs a = p.copy;
+        a.src = src;
+        a.dst = dst;
+        hipLaunchKernelGGL((k_copy<BIG>), dim3((unsigned)cap_grid(p.grid, 256)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    case TPL_KERNEL_QUAD: {
+        QuadArgs a = p.quad;
+        a.src = src;
+        a.dst = dst;
+        int64_t grid = (a.nquads + 64 * kQuadUnroll - 1) / (64 * kQuadUnroll);
+        hipLaunchKernelGGL((k_quad<kQuadUnroll, BIG>), dim3((unsigned)cap_grid(grid, 256)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    case TPL_KERNEL_LDS: {
+        Plan q = p;
+        q.lds.src = src;
+        q.lds.dst = dst;
+        return launch_lds<BIG>(q, st);
+    }
+    case TPL_KERNEL_REG16: {
+        Reg16Args a = p.reg16;
+        a.src = src;
+        a.dst = dst;
+        hipLaunchKernelGGL((k_reg16<BIG>), dim3((unsigned)cap_grid(p.grid, 256)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    default:
+        return hipSuccess;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Plan cache and error text.
+
+static thread_local std::string g_last_error;
+
+static int fail(int status, const std::string& why) {
+    g_last_error = why;
+    return status;
+}
+
+struct PlanCache {
+    std::mutex mu;
+    std::unordered_map<std::string, Plan> map;
+};
+
+static PlanCache& cache() {
+    static PlanCache c;
+    return c;
+}
+
+static bool log_enabled() {
+    static int on = -1;
+    if (on < 0) {
+        const char* e = getenv("TPL_LOG");
+        on = (e && *e && *e != '0') ? 1 : 0;
+    }
+    return on == 1;
+}
+
+static const char* kernel_name(int k) {
+    switch (k) {
+    case TPL_KERNEL_GATHER: return "gather";
+    case TPL_KERNEL_QUAD: return "quad";
+    case TPL_KERNEL_LDS: return "lds";
+    case TPL_KERNEL_REG16: return "reg16";
+    case TPL_KERNEL_COPY: return "copy";
+    default: return "none";
+    }
+}
+
+static Plan get_plan(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                     const int64_t* offs, int64_t batch, int sa, int da) {
+    std::string key;
+    key.reserve(64 + rank * 24);
+    auto put = [&](int64_t x) { key.append(reinterpret_cast<const char*>(&x), sizeof x); };
+    put(w);
+    put(rank);
+    for (int i = 0; i < rank; ++i) {
+        put(ext[i]);
+        put(ss[i]);
+        put(ds[i]);
+    }
+    put(offs[0]);
+    put(offs[1]);
+    put(batch);
+    put(sa);
+    put(da);
+    PlanCache& c = cache();
+    {
+        std::lock_guard<std::mutex> lk(c.mu);
+        auto it = c.map.find(key);
+        if (it != c.map.end()) return it->second;
+    }
+    Plan p = plan_gfx950(w, rank, ext, ss, ds, offs, batch, sa, da);
+    if (log_enabled()) {
+        std::fprintf(stderr, "[tpl] plan w=%d kernel=%s status=%d shard=", w, kernel_name(p.kernel), p.status);
+        for (int i = 0; i < p.shard.rank; ++i)
+            std::fprintf(stderr, "(%lld:%lld,%lld)", (long long)p.shard.m[i].e, (long long)p.shard.m[i].s,
+                         (long long)p.shard.m[i].d);
+        std::fprintf(stderr, " P=%lld k=%d shift=%d mask=%d k_w=%d shift_w=%d tile=%dx%d pitch=%d grid=%lld block=%lld\n",
+                     (long long)p.P, p.k, p.shift, p.mask, p.k_w, p.shift_w, p.tile_b, p.tile_a, p.pitch,
+                     (long long)p.grid, (long long)p.block);
+    }
+    std::lock_guard<std::mutex> lk(c.mu);
+    if (c.map.size() > 4096) c.map.clear();
+    c.map.emplace(key, p);
+    return p;
+}
+
+static int ptr_align(const void* p) {
+    uintptr_t x = (uintptr_t)p;
+    int a = 1;
+    while (a < 256 && (x % (2 * a)) == 0) a *= 2;
+    return a;
+}
+
+static int64_t cosize_side(const Shard& sh, bool src) {
+    int64_t c = 1;
+    for (int i = 0; i < sh.rank; ++i) c += (sh.m[i].e - 1) * (src ? sh.m[i].s : sh.m[i].d);
+    return c;
+}
+
+// Overlap is allowed only unit-for-unit: both sides start at one address,
+// every batch item is moved by one work unit that reads all before writing
+// (the planner's unit_is_item), items sit at the same offsets on both sides
+// and do not overlap each other, and an item covers the same span on both
+// sides.
+static bool inplace_ok(const Plan& p, const uint8_t* s, const uint8_t* d) {
+    if (s != d || !p.unit_is_item) return false;
+    const Shard& sh = p.shard;
+    int64_t in_s = 1, in_d = 1;
+    int others = 0;
+    int64_t ostride = 0;
+    for (int i = 0; i < sh.rank; ++i) {
+        if (i == p.mode_a || i == p.mode_b) {
+            in_s += (sh.m[i].e - 1) * sh.m[i].s;
+            in_d += (sh.m[i].e - 1) * sh.m[i].d;
+        } else {
+            if (sh.m[i].s != sh.m[i].d) return false;
+            ++others;
+            ostride = sh.m[i].s;
+        }
+    }
+    if (others > 1) return false;
+    if (in_s != in_d) return false;
+    if (others == 1 && ostride < in_s) return false;
+    return true;
+}
+
+static int permute_impl(const void* src, void* dst, int w, int rank, const int64_t* ext,
+                        const int64_t* ss, const int64_t* ds, const int64_t* offs_in, int64_t batch,
+                        hipStream_t stream) {
+    if (rank < 1 || rank > TPL_MAX_RANK) return fail(TPL_E_ARG, "rank must be in 1..8");
+    if (!ext || !ss || !ds) return fail(TPL_E_ARG, "extents/strides arrays must not be NULL");
+    if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16)
+        return fail(TPL_E_DTYPE_WIDTH, "unsupported dtype byte width (must be 1, 2, 4, 8 or 16)");
+    if (batch < 0) return fail(TPL_E_ARG, "batch must be >= 0");
+    for (int i = 0; i < rank; ++i)
+        if (ext[i] < 0) return fail(TPL_E_ARG, "extents must be >= 0");
+    int64_t n = 0;
+    if (!count_elements(rank, ext, batch, &n))
+        return fail(TPL_E_LAYOUT, "layouts must slice/canonicalize: element count overflows 64-bit addressing");
+    static const int64_t zero[2] = {0, 0};
+    const int64_t* offs = offs_in ? offs_in : zero;
+    if (n == 0) return TPL_OK;
+    if (!src || !dst) return fail(TPL_E_ARG, "src and dst must not be NULL");
+
+    const uint8_t* s = reinterpret_cast<const uint8_t*>(src);
+    uint8_t* d = reinterpret_cast<uint8_t*>(dst);
+    Plan p = get_plan(w, rank, ext, ss, ds, offs, batch, ptr_align(src), ptr_align(dst));
+    if (p.status != TPL_OK) return fail(p.status, p.reason);
+    if (p.kernel == TPL_KERNEL_NONE) return TPL_OK;
+
+    const uint8_t* sb = s + p.src_off_bytes;
+    uint8_t* db = d + p.dst_off_bytes;
+    const uint8_t* s_hi = sb + cosize_side(p.shard, true) * w;
+    const uint8_t* d_hi = db + cosize_side(p.shard, false) * w;
+    if (sb < d_hi && db < s_hi && !inplace_ok(p, sb, db))
+        return fail(TPL_E_ALIAS, "source and destination overlap other than unit-for-unit in place");
+
+    hipError_t e = p.big ? launch_big<true>(p, sb, db, stream) : launch_big<false>(p, sb, db, stream);
+    if (e != hipSuccess) return fail(TPL_E_HIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
+    return TPL_OK;
+}
+
+}  // namespace tpl
+
+// ---------------------------------------------------------------------------
+// C ABI.
+
+extern "C" {
+
+int tpl_permute(const void* src, void* dst, int dtype_bytes, int rank, const int64_t* extents,
+                const int64_t* src_strides, const int64_t* dst_strides, const int64_t* elem_offsets,
+                int64_t batch, hipStream_t stream) {
+    try {
+        return tpl::permute_impl(src, dst, dtype_bytes, rank, extents, src_strides, dst_strides,
+                                 elem_offsets, batch, stream);
+    } catch (...) {
+        return tpl::fail(TPL_E_ARG, "internal error");
+    }
+}
+
+int tpl_plan(int dtype_bytes, int rank, const int64_t* extents, const int64_t* src_strides,
+             const int64_t* dst_strides, const int64_t* elem_offsets, int64_t batch, int geometry,
+             tpl_plan_info* out) {
+    try {
+        tpl::Plan p;
+        if (rank < 1 || rank > TPL_MAX_RANK || !extents || !src_strides || !dst_strides || batch < 0) {
+            p.status = TPL_E_ARG;
+            p.reason = "rank must be in 1..8, arrays non-NULL, batch >= 0";
+        } else if (geometry == TPL_GEOM_PAGES32) {
+            p = tpl::plan_pages32(dtype_bytes, rank, extents, src_strides, dst_strides, batch);
+        } else if (geometry == TPL_GEOM_GFX950) {
+            static const int64_t zero[2] = {0, 0};
+            p = tpl::plan_gfx950(dtype_bytes, rank, extents, src_strides, dst_strides,
+                                 elem_offsets ? elem_offsets : zero, batch, 256, 256);
+            if (p.kernel == TPL_KERNEL_QUAD && p.status == TPL_OK)
+                p.grid = (p.quad.nquads + 64 * tpl::kQuadUnroll - 1) / (64 * tpl::kQuadUnroll);
+        } else {
+            p.status = TPL_E_ARG;
+            p.reason = "unknown geometry";
+        }
+        if (out) tpl::fill_info(p, out);
+        if (p.status != TPL_OK) return tpl::fail(p.status, p.reason);
+        return TPL_OK;
+    } catch (...) {
+        return tpl::fail(TPL_E_ARG, "internal error");
+    }
+}
+
+const char* tpl_status_string(int status) {
+    switch (status) {
+    case TPL_OK: return "ok";
+    case TPL_E_ARG: return "invalid argument";
+    case TPL_E_DTYPE_WIDTH: return "unsupported dtype byte width";
+    case TPL_E_DTYPE: return "dtype mismatch";
+    case TPL_E_EXTENT: return "extent mismatch";
+    case TPL_E_LAYOUT: return "layouts must slice/canonicalize";
+    case TPL_E_NO_K: return "no conflict-free XOR swizzle";
+    case TPL_E_ALIAS: return "source and destination overlap";
+    case TPL_E_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char* tpl_last_error(void) { return tpl::g_last_error.c_str(); }
+
+}  // extern "C"

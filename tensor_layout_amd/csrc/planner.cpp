@@ -1,0 +1,623 @@
+// planner.cpp -- host-side steps of permute_layout.
+//
+// permute_layout page, "Algorithm": (1) slice and canonicalise both layouts
+// and regroup them onto one shard, P = elements per lane; (2) choose the XOR
+// swizzle by simulating the banks of both staged phases and taking the
+// smallest k that is conflict-free, else decline; (3) the two register-staged
+// phases themselves, which here are the gfx950 kernels.  The operand rules
+// are those of the page's "What it accepts" section.
+#include "planner.hpp"
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <sstream>
+#include <unordered_map>
+
+namespace tpl {
+
+// ---------------------------------------------------------------------------
+// Bank geometries.
+
+static int log2_bytes(int bytes) {
+    int l = 0;
+    while ((1 << l) < bytes) ++l;
+    return l;
+}
+
+const Geometry& geometry_pages32() {
+    // The pages' warp: 32 lanes, 32 banks of 4 bytes, element-granular (two
+    // lanes in one bank conflict even inside one word).  An access of
+    // w > 4 bytes spans w/4 banks and the warp is served 128/w lanes at a time.
+    static const Geometry g = {
+        32, 4, false,
+        {32, 32, 32, 32, 32}, {32, 32, 32, 16, 8},
+        {32, 32, 32, 32, 32}, {32, 32, 32, 16, 8},
+    };
+    return g;
+}
+
+const Geometry& geometry_gfx950() {
+    // Measured on MI355X by timing ds_read/ds_write with chosen lane address
+    // patterns: b32 accesses see 32 banks of 4 bytes in two passes of 32
+    // lanes; ds_read_b64 sees 64 banks in passes of 32 lanes and
+    // ds_read_b128 64 banks in passes of 16 lanes; writes see 32 banks with
+    // passes of 32, 16 and 8 lanes for b32, b64 and b128.  Lanes reading the
+    // same dword are served together.  Sub-dword accesses are modelled as b32.
+    static const Geometry g = {
+        64, 4, true,
+        {32, 32, 32, 64, 64}, {32, 32, 32, 32, 16},
+        {32, 32, 32, 32, 32}, {32, 32, 32, 16, 8},
+    };
+    return g;
+}
+
+bool step_conflict_free(const Geometry& g, bool is_write, int bytes, const int64_t* addr,
+                        const bool* active, int lanes) {
+    int li = log2_bytes(bytes);
+    int banks = is_write ? g.banks_write[li] : g.banks_read[li];
+    int pass = is_write ? g.pass_write[li] : g.pass_read[li];
+    int words = bytes > g.bank_bytes ? bytes / g.bank_bytes : 1;
+    int64_t owner[64];
+    for (int p0 = 0; p0 < lanes; p0 += pass) {
+        for (int b = 0; b < banks; ++b) owner[b] = -1;
+        for (int l = p0; l < p0 + pass && l < lanes; ++l) {
+            if (active && !active[l]) continue;
+            int64_t w0 = addr[l] / g.bank_bytes;
+            for (int k = 0; k < words; ++k) {
+                int64_t word = w0 + k;
+                int bank = (int)(word % banks);
+                if (owner[bank] >= 0) {
+                    if (!(g.same_word_ok && owner[bank] == word)) return false;
+                }
+                owner[bank] = word;
+            }
+        }
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Canonical shard.
+
+Shard make_shard(int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                 int64_t batch) {
+    Mode tmp[kMaxShard];
+    int n = 0;
+    if (batch > 1) {
+        int64_t span_s = 1, span_d = 1;
+        for (int i = 0; i < rank; ++i) {
+            span_s += (ext[i] - 1) * ss[i];
+            span_d += (ext[i] - 1) * ds[i];
+        }
+        tmp[n++] = {batch, span_s, span_d};
+    }
+    for (int i = 0; i < rank; ++i)
+        if (ext[i] != 1) tmp[n++] = {ext[i], ss[i], ds[i]};
+    Shard sh;
+    if (n == 0) {
+        sh.rank = 1;
+        sh.m[0] = {1, 1, 1};
+        return sh;
+    }
+    // Neighbours i, i+1 merge when both sides see one longer run.
+    sh.m[0] = tmp[0];
+    sh.rank = 1;
+    for (int i = 1; i < n; ++i) {
+        Mode& last = sh.m[sh.rank - 1];
+        if (last.s == tmp[i].e * tmp[i].s && last.d == tmp[i].e * tmp[i].d) {
+            last.e *= tmp[i].e;
+            last.s = tmp[i].s;
+            last.d = tmp[i].d;
+        } else {
+            sh.m[sh.rank++] = tmp[i];
+        }
+    }
+    return sh;
+}
+
+bool dst_injective(const Shard& sh) {
+    // Sufficient test: sorted by destination stride, every stride exceeds the
+    // largest offset reachable with the smaller modes.
+    Mode m[kMaxShard];
+    int n = 0;
+    for (int i = 0; i < sh.rank; ++i)
+        if (sh.m[i].e > 1) m[n++] = sh.m[i];
+    std::sort(m, m + n, [](const Mode& a, const Mode& b) { return a.d < b.d; });
+    int64_t span = 0;
+    for (int i = 0; i < n; ++i) {
+        if (m[i].d <= span) return false;
+        span += (m[i].e - 1) * m[i].d;
+    }
+    return true;
+}
+
+static int64_t shard_elements(const Shard& sh) {
+    int64_t n = 1;
+    for (int i = 0; i < sh.rank; ++i) n *= sh.m[i].e;
+    return n;
+}
+
+static bool set_modes(Modes& out, const Shard& sh, const int* idx, int n) {
+    if (n > kMaxBatch) return false;
+    out.n = n;
+    for (int i = 0; i < n; ++i) {
+        const Mode& m = sh.m[idx[i]];
+        out.ext[i] = m.e;
+        out.ss[i] = m.s;
+        out.ds[i] = m.d;
+        out.div[i] = make_fastdiv((uint32_t)std::min<int64_t>(m.e, 0x7fffffff));
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// The pages' plan (32-lane warp program).
+
+static void decompose(int64_t n, const Shard& sh, int64_t* digits) {
+    for (int i = sh.rank - 1; i >= 0; --i) {
+        digits[i] = n % sh.m[i].e;
+        n /= sh.m[i].e;
+    }
+}
+
+Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                  int64_t batch) {
+    Plan p;
+    p.w = w;
+    if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) {
+        p.status = TPL_E_DTYPE_WIDTH;
+        p.reason = "unsupported dtype byte width";
+        return p;
+    }
+    for (int i = 0; i < rank; ++i) {
+        if (ext[i] < 1 || ss[i] < 0 || ds[i] < 0) {
+            p.status = TPL_E_LAYOUT;
+            p.reason = "layouts must slice/canonicalize: extents must be >= 1 and strides >= 0";
+            return p;
+        }
+    }
+    if (batch < 1) {
+        p.status = TPL_E_LAYOUT;
+        p.reason = "layouts must slice/canonicalize: batch must be >= 1";
+        return p;
+    }
+    p.shard = make_shard(rank, ext, ss, ds, batch);
+    if (!dst_injective(p.shard)) {
+        p.status = TPL_E_LAYOUT;
+        p.reason = "layouts must slice/canonicalize: destination is not one-to-one";
+        return p;
+    }
+    const Geometry& g = geometry_pages32();
+    const int lanes = g.lanes;
+    int64_t total = shard_elements(p.shard);
+    if (total % lanes) {
+        p.status = TPL_E_LAYOUT;
+        p.reason = "layouts must slice/canonicalize: elements are not a multiple of 32 lanes";
+        return p;
+    }
+    int64_t P = total / lanes;
+    p.P = P;
+    int kmax = 0;
+    while ((2ll << kmax) <= P && kmax < 5) ++kmax;
+    int64_t digits[kMaxShard];
+    int64_t addr[64];
+    for (int k = 0; k <= kmax; ++k) {
+        if (P % (1ll << k)) continue;
+        int mask = (1 << k) - 1, shift = 5 - k;
+        bool ok = true;
+        for (int phase = 0; phase < 2 && ok; ++phase) {
+            for (int64_t r = 0; r < P && ok; ++r) {
+                for (int lane = 0; lane < lanes; ++lane) {
+                    int64_t j = r ^ ((lane >> shift) & mask);
+                    decompose(lane + j * lanes, p.shard, digits);
+                    int64_t off = 0;
+                    for (int i = 0; i < p.shard.rank; ++i)
+                        off += digits[i] * (phase == 0 ? p.shard.m[i].s : p.shard.m[i].d);
+                    addr[lane] = off * w;
+                }
+                ok = step_conflict_free(g, phase == 1, w, addr, nullptr, lanes);
+            }
+        }
+        if (ok) {
+            p.k = k;
+            p.mask = mask;
+            p.shift = shift;
+            p.status = TPL_OK;
+            return p;
+        }
+    }
+    p.status = TPL_E_NO_K;
+    p.reason = "no XOR k makes both phases bank-conflict-free";
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// gfx950 LDS kernel: choose the pitch and the XOR of both LDS phases.
+
+struct LdsChoice {
+    bool ok = false;
+    int pitch = 0, ww = 0;
+    int k_w = 0, shift_w = 0, k_r = 0, shift_r = 0;
+};
+
+// Smallest k (then largest shift) whose XOR makes every step of a phase
+// conflict-free over every wave of the workgroup.
+template <typename AddrFn>
+static bool choose_phase(const Geometry& g, bool is_write, int bytes, int steps, int slots,
+                         int threads, AddrFn addr_of, int* k_out, int* shift_out) {
+    int kmax = 0;
+    while ((2 << kmax) <= steps) ++kmax;
+    int64_t addr[64];
+    for (int k = 0; k <= kmax; ++k) {
+        if (steps % (1 << k)) continue;
+        int mask = (1 << k) - 1;
+        for (int shift = 6 - k; shift >= 0; --shift) {
+            bool ok = true;
+            for (int wv = 0; wv < threads / kWave && ok; ++wv)
+                for (int slot = 0; slot < slots && ok; ++slot)
+                    for (int r = 0; r < steps && ok; ++r) {
+                        for (int l = 0; l < kWave; ++l)
+                            addr[l] = addr_of(wv * kWave + l, slot, r, shift, mask);
+                        ok = step_conflict_free(g, is_write, bytes, addr, nullptr, kWave);
+                    }
+            if (ok) {
+                *k_out = k;
+                *shift_out = shift;
+                return true;
+            }
+            if (k == 0) break;   // with mask 0 the shift does not matter
+        }
+    }
+    return false;
+}
+
+static LdsChoice choose_lds(const LdsShape& sh) {
+    const Geometry& g = geometry_gfx950();
+    const int row = sh.row_bytes();
+    const int pads[] = {16, 8, 4, 0, 32, 48, 64};
+    for (int pad : pads) {
+        int pitch = row + pad;
+        int ww = (pitch % 16 == 0) ? 16 : (pitch % 8 == 0) ? 8 : 4;
+        if (sh.tb * pitch > 64 * 1024) continue;
+        LdsChoice c;
+        c.pitch = pitch;
+        c.ww = ww;
+        bool okw = choose_phase(
+            g, true, ww, 16 / ww, 4, sh.threads(),
+            [&](int t, int slot, int r, int shift, int mask) {
+                return (int64_t)lds_write_addr(sh, pitch, ww, t, slot, r, shift, mask, nullptr);
+            },
+            &c.k_w, &c.shift_w);
+        if (!okw) continue;
+        bool okr = choose_phase(
+            g, false, sh.read_bytes(), sh.reads_per_group(), sh.groups_per_thread(), sh.threads(),
+            [&](int t, int slot, int r, int shift, int mask) {
+                return (int64_t)lds_read_addr(sh, pitch, t, slot, r, shift, mask, nullptr);
+            },
+            &c.k_r, &c.shift_r);
+        if (!okr) continue;
+        c.ok = true;
+        return c;
+    }
+    return LdsChoice{};
+}
+
+// Tile shapes the library instantiates: (w, TB, TA), largest first.
+static const LdsShape kLdsShapes[] = {
+    {1, 128, 128}, {1, 64, 128},
+    {2, 128, 64}, {2, 32, 64},
+    {4, 64, 64}, {4, 32, 32},
+    {8, 32, 64}, {8, 16, 32},
+};
+
+const LdsShape* lds_shapes(int* n) {
+    *n = (int)(sizeof(kLdsShapes) / sizeof(kLdsShapes[0]));
+    return kLdsShapes;
+}
+
+static std::mutex g_choice_mu;
+
+static LdsChoice cached_choice(const LdsShape& sh) {
+    static std::unordered_map<int, LdsChoice> cache;
+    int key = sh.w * 1000000 + sh.tb * 1000 + sh.ta;
+    std::lock_guard<std::mutex> lk(g_choice_mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    LdsChoice c = choose_lds(sh);
+    cache[key] = c;
+    return c;
+}
+
+// ---------------------------------------------------------------------------
+// Device plan.
+
+static int pow2_align(int64_t x) {
+    // largest power of two (<= 256) dividing x (x == 0 counts as 256)
+    int a = 1;
+    while (a < 256 && (x % (2 * a)) == 0) a *= 2;
+    return a;
+}
+
+static bool all_aligned(const Shard& sh, int skip_a, int skip_b, int w, bool src_side, int align) {
+    for (int i = 0; i < sh.rank; ++i) {
+        int64_t st = src_side ? sh.m[i].s : sh.m[i].d;
+        if (i == skip_a || i == skip_b) continue;
+        if ((st * w) % align) return false;
+    }
+    return true;
+}
+
+bool count_elements(int rank, const int64_t* ext, int64_t batch, int64_t* out) {
+    // Product of the extents and the batch; false when it exceeds 2^62
+    // (a zero extent anywhere makes the product 0 and is never an overflow).
+    bool zero = batch == 0;
+    for (int i = 0; i < rank; ++i) zero = zero || ext[i] == 0;
+    if (zero) {
+        *out = 0;
+        return true;
+    }
+    __int128 n = batch;
+    for (int i = 0; i < rank; ++i) {
+        n *= ext[i];
+        if (n > ((__int128)1 << 62)) return false;
+    }
+    *out = (int64_t)n;
+    return true;
+}
+
+Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                 const int64_t* offs, int64_t batch, int src_align, int dst_align) {
+    Plan p;
+    p.w = w;
+    if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) {
+        p.status = TPL_E_DTYPE_WIDTH;
+        p.reason = "unsupported dtype byte width (must be 1, 2, 4, 8 or 16)";
+        return p;
+    }
+    int64_t n = 0;
+    if (!count_elements(rank, ext, batch, &n)) {
+        p.status = TPL_E_LAYOUT;
+        p.reason = "layouts must slice/canonicalize: element count overflows 64-bit addressing";
+        return p;
+    }
+    if (n == 0) {
+        p.kernel = TPL_KERNEL_NONE;
+        p.shard.rank = 0;
+        return p;
+    }
+    for (int i = 0; i < rank; ++i) {
+        if (ss[i] < 0 || ds[i] < 0) {
+            p.status = TPL_E_LAYOUT;
+            p.reason = "layouts must slice/canonicalize: negative strides are not supported";
+            return p;
+        }
+    }
+    if (offs[0] < 0 || offs[1] < 0) {
+        p.status = TPL_E_LAYOUT;
+        p.reason = "layouts must slice/canonicalize: negative element offsets";
+        return p;
+    }
+    // Overflow: the largest byte offset on each side must fit comfortably.
+    const int64_t lim = (int64_t)1 << 58;
+    for (int side = 0; side < 2; ++side) {
+        long double span = 1;
+        for (int i = 0; i < rank; ++i) span += (long double)(ext[i] - 1) * (side ? ds[i] : ss[i]);
+        long double hi = ((long double)offs[side] + (long double)batch * span) * w;
+        if (hi > (long double)lim) {
+            p.status = TPL_E_LAYOUT;
+            p.reason = "layouts must slice/canonicalize: offsets overflow 64-bit addressing";
+            return p;
+        }
+    }
+    p.shard = make_shard(rank, ext, ss, ds, batch);
+    const Shard& sh = p.shard;
+    if (!dst_injective(sh)) {
+        p.status = TPL_E_LAYOUT;
+        p.reason = "layouts must slice/canonicalize: destination layout is not one-to-one";
+        return p;
+    }
+    p.src_off_bytes = offs[0] * w;
+    p.dst_off_bytes = offs[1] * w;
+    int sa = std::min(src_align, pow2_align(p.src_off_bytes));
+    int da = std::min(dst_align, pow2_align(p.dst_off_bytes));
+    p.big = n >= ((int64_t)1 << 31);
+    int64_t max_off = 0;
+    for (int i = 0; i < sh.rank; ++i)
+        max_off = std::max(max_off, (sh.m[i].e - 1) * std::max(sh.m[i].s, sh.m[i].d));
+    if (max_off >= ((int64_t)1 << 31)) p.big = true;
+
+    // The two contiguous modes.
+    int a = -1, b = -1;
+    for (int i = 0; i < sh.rank; ++i) {
+        if (sh.m[i].e > 1 && sh.m[i].s == 1) a = i;
+        if (sh.m[i].e > 1 && sh.m[i].d == 1) b = i;
+    }
+    p.mode_a = a;
+    p.mode_b = b;
+    int others[kMaxShard];
+    int no = 0;
+    for (int i = 0; i < sh.rank; ++i)
+        if (i != a && i != b) others[no++] = i;
+
+    auto choose_gather = [&]() {
+        p.kernel = TPL_KERNEL_GATHER;
+        int unit = w;
+        while (unit > 1 && ((sa % unit) || (da % unit))) unit /= 2;
+        int idx[kMaxShard];
+        for (int i = 0; i < sh.rank; ++i) idx[i] = i;
+        GatherArgs& ga = p.gather;
+        set_modes(ga.modes, sh, idx, sh.rank);
+        ga.total = n;
+        ga.unit = unit;
+        ga.w = w;
+        p.P = 1;
+        p.block = 256;
+        p.grid = std::min<int64_t>((n + 255) / 256, 1 << 16);
+        if (p.big) p.grid = std::min<int64_t>(p.grid, 1 << 15);
+    };
+
+    // 16-byte elements: one element is one dwordx4; lanes form 8x8 blocks.
+    if (w == 16 && a >= 0 && b >= 0 && a != b && sa % 16 == 0 && da % 16 == 0) {
+        p.kernel = TPL_KERNEL_REG16;
+        Reg16Args& r = p.reg16;
+        r.e_b = sh.m[b].e;
+        r.e_a = sh.m[a].e;
+        r.s_b = sh.m[b].s;
+        r.d_a = sh.m[a].d;
+        r.nbb = (r.e_b + 7) / 8;
+        r.nba = (r.e_a + 7) / 8;
+        int64_t items = 1;
+        for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
+        r.nblocks = items * r.nbb * r.nba;
+        if (r.nblocks >= ((int64_t)1 << 31)) p.big = true;
+        r.div_nba = make_fastdiv((uint32_t)std::min<int64_t>(r.nba, 0x7fffffff));
+        r.div_nbb = make_fastdiv((uint32_t)std::min<int64_t>(r.nbb, 0x7fffffff));
+        set_modes(r.batch, sh, others, no);
+        p.P = 1;
+        p.tile_b = 8;
+        p.tile_a = 8;
+        p.block = 256;
+        p.grid = (r.nblocks + 3) / 4;
+        p.unit_is_item = (r.nbb == 1 && r.nba == 1);
+        return p;
+    }
+
+    // Both sides contiguous along the same mode: copy runs.
+    if (a >= 0 && a == b) {
+        int64_t run = sh.m[a].e * w;
+        if (run % 16 == 0 && sa % 16 == 0 && da % 16 == 0 && all_aligned(sh, a, -1, w, true, 16) &&
+            all_aligned(sh, a, -1, w, false, 16)) {
+            p.kernel = TPL_KERNEL_COPY;
+            CopyArgs& c = p.copy;
+            c.cpr = run / 16;
+            c.div_cpr = make_fastdiv((uint32_t)std::min<int64_t>(c.cpr, 0x7fffffff));
+            c.nchunks = n * w / 16;
+            c.w = w;
+            if (c.nchunks >= ((int64_t)1 << 31)) p.big = true;
+            set_modes(c.rows, sh, others, no);
+            p.P = 16 / w;
+            p.block = 256;
+            p.grid = std::min<int64_t>((c.nchunks + 255) / 256, 1 << 20);
+            return p;
+        }
+        choose_gather();
+        return p;
+    }
+
+    if (a >= 0 && b >= 0 && w <= 8) {
+        const Mode& ma = sh.m[a];
+        const Mode& mb = sh.m[b];
+        bool src_ok = sa % 16 == 0 && all_aligned(sh, a, -1, w, true, 16);
+        bool dst_ok = da % 16 == 0 && all_aligned(sh, b, -1, w, false, 16);
+        // 4x4 fp32 blocks transposed inside lane quads.
+        if (w == 4 && mb.e == 4 && ma.e % 4 == 0 && src_ok && dst_ok) {
+            p.kernel = TPL_KERNEL_QUAD;
+            QuadArgs& q = p.quad;
+            q.qpr = ma.e / 4;
+            q.div_qpr = make_fastdiv((uint32_t)std::min<int64_t>(q.qpr, 0x7fffffff));
+            q.s_b = mb.s;
+            q.d_a = ma.d;
+            int64_t items = 1;
+            for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
+            q.nquads = items * q.qpr;
+            if (q.nquads >= ((int64_t)1 << 31)) p.big = true;
+            set_modes(q.batch, sh, others, no);
+            p.P = 4;
+            p.tile_b = 4;
+            p.tile_a = (int)std::min<int64_t>(ma.e, 64);
+            p.block = 256;
+            // One quad block per lane quad; 64 quad blocks per workgroup per step.
+            p.grid = 0;  // set at launch (depends on the unroll)
+            // Each batch item is moved by one wave-instruction when its 4x4
+            // blocks fit one wave (16 quads) and tile the wave evenly.
+            p.unit_is_item = (q.qpr <= 16 && 16 % q.qpr == 0);
+            return p;
+        }
+        // Tiled LDS transpose.
+        if (ma.e * w >= 64 && mb.e * w >= 64 && src_ok && dst_ok) {
+            const LdsShape* pick = nullptr;
+            for (const LdsShape& s : kLdsShapes) {
+                if (s.w != w) continue;
+                if (s.tb <= mb.e && s.ta <= ma.e) {
+                    pick = &s;
+                    break;
+                }
+            }
+            if (!pick) {
+                for (const LdsShape& s : kLdsShapes)
+                    if (s.w == w) pick = &s;   // smallest of this width; partial tiles
+            }
+            LdsChoice c = cached_choice(*pick);
+            if (!c.ok) {
+                p.status = TPL_E_NO_K;
+                p.reason = "no XOR k makes both LDS phases bank-conflict-free for this tile";
+                return p;
+            }
+            p.kernel = TPL_KERNEL_LDS;
+            LdsArgs& l = p.lds;
+            l.e_b = mb.e;
+            l.e_a = ma.e;
+            l.s_b = mb.s;
+            l.d_a = ma.d;
+            l.ntb = (mb.e + pick->tb - 1) / pick->tb;
+            l.nta = (ma.e + pick->ta - 1) / pick->ta;
+            int64_t items = 1;
+            for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
+            l.ntiles = items * l.ntb * l.nta;
+            if (l.ntiles >= ((int64_t)1 << 31)) p.big = true;
+            l.div_nta = make_fastdiv((uint32_t)std::min<int64_t>(l.nta, 0x7fffffff));
+            l.div_ntb = make_fastdiv((uint32_t)std::min<int64_t>(l.ntb, 0x7fffffff));
+            set_modes(l.batch, sh, others, no);
+            l.pitch = c.pitch;
+            l.shift_r = c.shift_r;
+            l.mask_r = (1 << c.k_r) - 1;
+            l.shift_w = c.shift_w;
+            l.mask_w = (1 << c.k_w) - 1;
+            p.tile_b = pick->tb;
+            p.tile_a = pick->ta;
+            p.pitch = c.pitch;
+            p.ww = c.ww;
+            p.k = c.k_r;
+            p.shift = c.shift_r;
+            p.mask = l.mask_r;
+            p.k_w = c.k_w;
+            p.shift_w = c.shift_w;
+            p.mask_w = l.mask_w;
+            p.P = pick->reads_per_group();
+            p.block = pick->threads();
+            p.grid = l.ntiles;
+            p.lds_bytes = pick->tb * c.pitch;
+            p.unit_is_item = (l.ntb == 1 && l.nta == 1 && mb.e == pick->tb && ma.e == pick->ta);
+            return p;
+        }
+    }
+    choose_gather();
+    return p;
+}
+
+void fill_info(const Plan& p, tpl_plan_info* out) {
+    std::memset(out, 0, sizeof(*out));
+    out->status = p.status;
+    out->rank = p.shard.rank;
+    for (int i = 0; i < p.shard.rank && i < TPL_MAX_SHARD; ++i) {
+        out->extent[i] = p.shard.m[i].e;
+        out->src_str[i] = p.shard.m[i].s;
+        out->dst_str[i] = p.shard.m[i].d;
+    }
+    out->P = p.P;
+    out->k = p.k;
+    out->shift = p.shift;
+    out->mask = p.mask;
+    out->k_w = p.k_w;
+    out->shift_w = p.shift_w;
+    out->mask_w = p.mask_w;
+    out->kernel = p.kernel;
+    out->tile[0] = p.tile_b;
+    out->tile[1] = p.tile_a;
+    out->lds_pitch = p.pitch;
+    out->grid = p.grid;
+    out->block = p.block;
+}
+
+}  // namespace tpl

@@ -1,0 +1,85 @@
+// planner.hpp -- host-side steps of permute_layout: validation, canonical
+// shard, bank simulation and XOR-k choice, kernel selection, plan cache.
+#pragma once
+
+#include <stdint.h>
+#include <string>
+
+#include "common.hpp"
+#include "../../include/tpl.h"
+
+namespace tpl {
+
+struct Mode {
+    int64_t e, s, d;   // extent, source stride, destination stride (elements)
+};
+
+struct Shard {
+    int rank = 0;
+    Mode m[kMaxShard];
+};
+
+// One LDS access phase as the bank simulator sees it.
+struct Geometry {
+    int lanes;          // lanes per wave
+    int bank_bytes;     // bytes per bank
+    bool same_word_ok;  // lanes touching the same word do not conflict
+    // banks and lanes per pass for an access of `bytes` bytes (read or write)
+    int banks_read[5], pass_read[5];    // index: log2(bytes) - 0 (1,2,4,8,16)
+    int banks_write[5], pass_write[5];
+};
+
+const Geometry& geometry_pages32();
+const Geometry& geometry_gfx950();
+
+// Does one unrolled step (one access per lane) run without bank conflicts?
+// `addr` holds each lane's byte address, `bytes` the access width; lanes with
+// active[l] == false do not take part.
+bool step_conflict_free(const Geometry& g, bool is_write, int bytes, const int64_t* addr,
+                        const bool* active, int lanes);
+
+struct Plan {
+    int status = TPL_OK;
+    std::string reason;
+    Shard shard;            // canonical shard, batch folded in
+    int w = 0;
+    int kernel = TPL_KERNEL_NONE;
+    int64_t P = 0;
+    int k = 0, shift = 0, mask = 0;        // read phase (PAGES32: both phases)
+    int k_w = 0, shift_w = 0, mask_w = 0;  // LDS write phase
+    int tile_b = 0, tile_a = 0, pitch = 0, ww = 0;
+    int64_t grid = 0, block = 0;
+    int lds_bytes = 0;
+    bool big = false;       // 64-bit index math needed
+    bool unit_is_item = false;  // each batch item is moved by one work unit (reads before writes)
+    int mode_a = -1, mode_b = -1;          // shard indices of the two contiguous modes
+    int64_t src_off_bytes = 0, dst_off_bytes = 0;
+    // kernel arguments (pointers filled at launch)
+    GatherArgs gather{};
+    CopyArgs copy{};
+    QuadArgs quad{};
+    LdsArgs lds{};
+    Reg16Args reg16{};
+};
+
+// Full planning for the device path.  src_align / dst_align: alignment in
+// bytes of the base pointers (after elem_offsets are applied).
+Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                 const int64_t* offs, int64_t batch, int src_align, int dst_align);
+
+// The pages' method on one warp region (32 lanes, 32 banks).
+Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                  int64_t batch);
+
+// Canonical shard (unit modes dropped, neighbours merged where both sides merge).
+Shard make_shard(int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                 int64_t batch);
+
+bool dst_injective(const Shard& sh);
+
+// Element count batch * prod(ext); false on overflow past 2^62.
+bool count_elements(int rank, const int64_t* ext, int64_t batch, int64_t* out);
+
+void fill_info(const Plan& p, tpl_plan_info* out);
+
+}  // namespace tpl

@@ -1,0 +1,207 @@
+"""Thin ctypes binding of libtpl.so (argument marshalling only).
+
+The names follow the C ABI in include/tpl.h: ``tpl_permute``, ``tpl_plan``,
+``tpl_status_string`` and ``tpl_last_error``.  ``permute`` is a convenience
+wrapper over torch tensors: it checks dtypes, extents and byte ranges, then
+calls ``tpl_permute`` on the tensors' device pointers and torch's current
+stream.  Every step of the permutation runs in the library's HIP kernels; if
+the library is missing or cannot be loaded every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtpl.so")
+
+TPL_OK = 0
+TPL_E_ARG = 1
+TPL_E_DTYPE_WIDTH = 2
+TPL_E_DTYPE = 3
+TPL_E_EXTENT = 4
+TPL_E_LAYOUT = 5
+TPL_E_NO_K = 6
+TPL_E_ALIAS = 7
+TPL_E_HIP = 8
+
+TPL_GEOM_GFX950 = 0
+TPL_GEOM_PAGES32 = 1
+
+KERNELS = {0: "none", 1: "gather", 2: "quad", 3: "lds", 4: "reg16", 5: "copy"}
+MAX_SHARD = 10
+
+EXPORTED = ("tpl_permute", "tpl_plan", "tpl_status_string", "tpl_last_error")
+
+
+class TplError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("status", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("extent", ctypes.c_int64 * MAX_SHARD),
+        ("src_str", ctypes.c_int64 * MAX_SHARD),
+        ("dst_str", ctypes.c_int64 * MAX_SHARD),
+        ("P", ctypes.c_int64),
+        ("k", ctypes.c_int32),
+        ("shift", ctypes.c_int32),
+        ("mask", ctypes.c_int32),
+        ("k_w", ctypes.c_int32),
+        ("shift_w", ctypes.c_int32),
+        ("mask_w", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
+        ("tile", ctypes.c_int32 * 2),
+        ("lds_pitch", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("block", ctypes.c_int64),
+    ]
+
+
+@dataclass
+class PlanInfo:
+    status: int
+    reason: str
+    extent: List[int] = field(default_factory=list)
+    src_str: List[int] = field(default_factory=list)
+    dst_str: List[int] = field(default_factory=list)
+    P: int = 0
+    k: int = 0
+    shift: int = 0
+    mask: int = 0
+    k_w: int = 0
+    shift_w: int = 0
+    mask_w: int = 0
+    kernel: str = "none"
+    tile: tuple = (0, 0)
+    lds_pitch: int = 0
+    grid: int = 0
+    block: int = 0
+
+    @property
+    def ok(self) -> bool:
+        return self.status == TPL_OK
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libtpl.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first (python -c 'import __graft_entry__ as g; g.build()')")
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7, and a
+    # library loaded before torch would pull in a second copy from /opt/rocm.
+    # Loading torch first makes libtpl.so bind to torch's runtime, so device
+    # pointers and stream handles from torch are valid in the library.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.tpl_permute.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                i64p, i64p, i64p, i64p, ctypes.c_int64, ctypes.c_void_p]
+    lib.tpl_permute.restype = ctypes.c_int
+    lib.tpl_plan.argtypes = [ctypes.c_int, ctypes.c_int, i64p, i64p, i64p, i64p, ctypes.c_int64,
+                             ctypes.c_int, ctypes.POINTER(_PlanInfo)]
+    lib.tpl_plan.restype = ctypes.c_int
+    lib.tpl_status_string.argtypes = [ctypes.c_int]
+    lib.tpl_status_string.restype = ctypes.c_char_p
+    lib.tpl_last_error.argtypes = []
+    lib.tpl_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _arr(xs: Sequence[int]):
+    return (ctypes.c_int64 * max(1, len(xs)))(*[int(x) for x in xs])
+
+
+def tpl_status_string(status: int) -> str:
+    return load().tpl_status_string(int(status)).decode()
+
+
+def tpl_last_error() -> str:
+    return load().tpl_last_error().decode()
+
+
+def tpl_permute(src_ptr: int, dst_ptr: int, dtype_bytes: int, extents: Sequence[int],
+                src_strides: Sequence[int], dst_strides: Sequence[int],
+                elem_offsets: Sequence[int] = (0, 0), batch: int = 1, stream: int = 0) -> int:
+    """Call the C entry point on raw device pointers; returns the status code."""
+    lib = load()
+    return lib.tpl_permute(ctypes.c_void_p(src_ptr), ctypes.c_void_p(dst_ptr), int(dtype_bytes),
+                           len(extents), _arr(extents), _arr(src_strides), _arr(dst_strides),
+                           _arr(elem_offsets), int(batch), ctypes.c_void_p(stream))
+
+
+def tpl_plan(dtype_bytes: int, extents: Sequence[int], src_strides: Sequence[int],
+             dst_strides: Sequence[int], elem_offsets: Optional[Sequence[int]] = None,
+             batch: int = 1, geometry: int = TPL_GEOM_GFX950) -> PlanInfo:
+    """Host-only planning (no GPU needed)."""
+    lib = load()
+    info = _PlanInfo()
+    offs = _arr(elem_offsets) if elem_offsets is not None else None
+    st = lib.tpl_plan(int(dtype_bytes), len(extents), _arr(extents), _arr(src_strides),
+                      _arr(dst_strides), offs, int(batch), int(geometry), ctypes.byref(info))
+    reason = tpl_last_error() if st != TPL_OK else ""
+    r = info.rank
+    return PlanInfo(st, reason, list(info.extent[:r]), list(info.src_str[:r]), list(info.dst_str[:r]),
+                    info.P, info.k, info.shift, info.mask, info.k_w, info.shift_w, info.mask_w,
+                    KERNELS.get(info.kernel, "?"), (info.tile[0], info.tile[1]), info.lds_pitch,
+                    info.grid, info.block)
+
+
+def _cosize(extents, strides):
+    if any(e == 0 for e in extents):
+        return 0
+    return 1 + sum((e - 1) * s for e, s in zip(extents, strides))
+
+
+def permute(dst, src, extents: Sequence[int], src_strides: Sequence[int], dst_strides: Sequence[int],
+            src_offset: int = 0, dst_offset: int = 0, batch: int = 1, dtype_bytes: Optional[int] = None,
+            stream=None) -> None:
+    """Permute ``src`` into ``dst`` (torch tensors on the GPU, used as flat storage).
+
+    Argument order is (dst, src) as in the pages' ``permute_layout(dst, src)``.
+    Strides and offsets are in elements of ``dtype_bytes`` bytes (default: the
+    tensors' element size).  Raises TplError on any non-OK status.
+    """
+    import torch
+
+    if src.dtype != dst.dtype and dtype_bytes is None:
+        raise TplError(TPL_E_DTYPE, "dtype mismatch")
+    w = int(dtype_bytes or src.element_size())
+    if not (src.is_cuda and dst.is_cuda):
+        raise TplError(TPL_E_ARG, "tensors must live on the GPU")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise TplError(TPL_E_ARG, "tensors must be contiguous storage")
+    if not (len(extents) == len(src_strides) == len(dst_strides)):
+        raise TplError(TPL_E_EXTENT, "extent mismatch")
+    n = batch
+    for e in extents:
+        n *= e
+    if n > 0:
+        need_s = (src_offset + batch * _cosize(extents, src_strides)) * w
+        need_d = (dst_offset + batch * _cosize(extents, dst_strides)) * w
+        if need_s > src.numel() * src.element_size() or need_d > dst.numel() * dst.element_size():
+            raise TplError(TPL_E_ARG, "layout reaches past the end of a tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = tpl_permute(src.data_ptr(), dst.data_ptr(), w, extents, src_strides, dst_strides,
+                     (src_offset, dst_offset), batch, sp)
+    if st != TPL_OK:
+        raise TplError(st, tpl_last_error())

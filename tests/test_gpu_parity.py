@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, byte for byte.
+
+Every case prints its name before touching the GPU.  Destinations start
+filled with the sentinel byte 0xA5 so that a missed or stray write shows up as
+a difference from the oracle, which sees the same sentinel.
+"""
+
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from tensor_layout_amd import synth, tpl, workloads
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xA5
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def cosize(extents, strides):
+    if any(e == 0 for e in extents):
+        return 0
+    return 1 + sum((e - 1) * s for e, s in zip(extents, strides))
+
+
+def sizes(w, ext, ss, ds, offs, batch):
+    ns = offs[0] + batch * cosize(ext, ss)
+    nd = offs[1] + batch * cosize(ext, ds)
+    return ns * w, nd * w
+
+
+def make_input(seed, nbytes, specials=False, w=4):
+    x = synth.random_bytes(seed, nbytes).copy()
+    if specials and w == 4:
+        synth.inject_f32_specials(x.view(np.uint32), seed ^ 0x5EC1A1)
+    return x
+
+
+def run_case(name, w, ext, ss, ds, offs=(0, 0), batch=1, seed=1, specials=False, expect_kernel=None):
+    torch = _torch()
+    print(f"\n[case] {name}: w={w} ext={tuple(ext)} ss={tuple(ss)} ds={tuple(ds)} offs={tuple(offs)} batch={batch}",
+          flush=True)
+    nbs, nbd = sizes(w, ext, ss, ds, offs, batch)
+    x = make_input(seed, nbs, specials, w)
+    ref = np.full(nbd, SENTINEL, dtype=np.uint8)
+    oracle.permute(x, ref, w, ext, ss, ds, offs, batch)
+    s = torch.from_numpy(x).cuda()
+    d = torch.full((max(nbd, 1),), SENTINEL, dtype=torch.uint8, device="cuda")
+    if expect_kernel is not None:
+        plan = tpl.tpl_plan(w, ext, ss, ds, offs, batch)
+        assert plan.kernel == expect_kernel, plan
+    tpl.permute(d, s, ext, ss, ds, offs[0], offs[1], batch, dtype_bytes=w)
+    torch.cuda.synchronize()
+    got = d.cpu().numpy()[:nbd]
+    if not np.array_equal(got, ref):
+        diff = np.flatnonzero(got != ref)
+        raise AssertionError(f"{name}: {diff.size} bytes differ; first at byte {diff[0]}")
+    return got
+
+
+# ---------------------------------------------------------------------------
+# the workloads, on sizes the oracle finishes in well under a second
+
+
+SMALL = [
+    workloads.SF_WORKED,
+    workloads.scaled(workloads.SF_BATCHED, batch=8192),
+    workloads.scaled(workloads.TILE_128x64, batch=64),
+    workloads.scaled(workloads.mixed_width(1), extents=(2, 128, 32, 32)),
+    workloads.scaled(workloads.mixed_width(2), extents=(2, 128, 32, 32)),
+    workloads.scaled(workloads.mixed_width(4), extents=(2, 128, 32, 32)),
+    workloads.scaled(workloads.mixed_width(8), extents=(2, 128, 32, 32)),
+    workloads.Workload("transpose_1024x768_bf16", 2, (1024, 768), (768, 1), (1, 1024), seed=0x5EED0050),
+    workloads.Workload("transpose_256x192_16B", 16, (256, 192), (192, 1), (1, 256), seed=0x5EED0051),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_workload_small(wl):
+    run_case(wl.name, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+             wl.seed, wl.specials)
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size, in the launch configuration the benchmark times
+
+
+@pytest.mark.parametrize("wl", workloads.ALL, ids=lambda w: w.name)
+def test_workload_full_size(wl):
+    run_case(wl.name, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+             wl.seed, wl.specials)
+
+
+# ---------------------------------------------------------------------------
+# ragged tails, several tiles, every kernel family
+
+
+RAGGED = [
+    # (name, w, extents, src strides, dst strides, expected kernel); rows padded to 16 bytes
+    ("lds_w1_ragged", 1, (3, 200, 333), (200 * 336, 336, 1), (333 * 208, 1, 208), "lds"),
+    ("lds_w2_ragged", 2, (2, 130, 1000), (130 * 1000, 1000, 1), (1000 * 136, 1, 136), "lds"),
+    ("lds_w4_ragged", 4, (3, 70, 130), (70 * 132, 132, 1), (130 * 72, 1, 72), "lds"),
+    ("lds_w8_ragged", 8, (2, 33, 65), (33 * 66, 66, 1), (65 * 34, 1, 34), "lds"),
+    ("lds_w2_small_tile", 2, (96, 160), (168, 1), (1, 104), "lds"),
+    ("lds_w1_small_tile", 1, (80, 144), (160, 1), (1, 96), "lds"),
+    ("reg16_ragged", 16, (13, 27), (27, 1), (1, 13), "reg16"),
+    ("quad_qpr9", 4, (4, 36), (36, 1), (1, 4), "quad"),
+    ("quad_padded", 4, (5, 4, 32), (160, 40, 1), (256, 1, 8), "quad"),
+    ("copy_outer_perm", 4, (8, 64, 32), (32, 256, 1), (2048, 32, 1), "copy"),
+    ("copy_identity", 2, (1000, 64), (64, 1), (64, 1), "copy"),
+    ("gather_unaligned_rows", 2, (130, 1000), (1000, 1), (1, 130), "gather"),
+    ("gather_no_unit_stride", 4, (16, 24), (48, 2), (24, 1), "gather"),
+    ("gather_small_modes", 8, (3, 5, 7), (35, 7, 1), (1, 3, 15), "gather"),
+    ("lds_broadcast_src", 4, (64, 32), (0, 1), (1, 64), "lds"),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: c[0])
+def test_ragged_and_kernel_families(case):
+    name, w, ext, ss, ds, kernel = case
+    batch = 3 if kernel not in ("lds",) else 1
+    run_case(name, w, ext, ss, ds, seed=zlib.crc32(name.encode()) & 0xFFFF, expect_kernel=kernel, batch=batch)
+
+
+@pytest.mark.parametrize("w,offs", [(4, (3, 0)), (4, (0, 5)), (2, (1, 7)), (16, (1, 1)), (1, (3, 9))])
+def test_unaligned_offsets(w, offs):
+    """Offsets that break 16-byte alignment fall back to narrower accesses."""
+    ext = (4, 32) if w == 4 else (64, 48)
+    ss = (ext[1], 1)
+    ds = (1, ext[0])
+    run_case(f"unaligned_w{w}_{offs}", w, ext, ss, ds, offs, batch=5, seed=w * 31 + offs[0])
+
+
+def test_random_layouts():
+    rng = np.random.default_rng(99)
+    for t in range(24):
+        rank = int(rng.integers(1, 5))
+        w = int(rng.choice([1, 2, 4, 8, 16]))
+        ext = [int(rng.integers(1, 9)) for _ in range(rank)]
+        order = list(rng.permutation(rank))
+        ds = [0] * rank
+        acc = 1
+        for ax in reversed(order):
+            ds[ax] = acc
+            acc *= ext[ax] + int(rng.integers(0, 2))
+        ss = [int(rng.integers(0, 9)) for _ in range(rank)]
+        offs = (int(rng.integers(0, 4)), int(rng.integers(0, 4)))
+        run_case(f"random_{t}", w, ext, ss, ds, offs, batch=int(rng.integers(1, 4)), seed=t)
+
+
+# ---------------------------------------------------------------------------
+# in place, overlap, declines, empty
+
+
+def test_inplace_sf_transpose():
+    torch = _torch()
+    wl = workloads.SF_BATCHED
+    print("\n[case] inplace SF transpose, full size", flush=True)
+    n = wl.elements * 4
+    x = make_input(wl.seed, n, True)
+    ref = np.empty_like(x)
+    oracle.permute(x, ref, 4, wl.extents, wl.src_strides, wl.dst_strides, (0, 0), wl.batch)
+    buf = torch.from_numpy(x).cuda()
+    tpl.permute(buf, buf, wl.extents, wl.src_strides, wl.dst_strides, batch=wl.batch, dtype_bytes=4)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), ref)
+
+
+def test_inplace_tile_move():
+    torch = _torch()
+    wl = workloads.scaled(workloads.TILE_128x64, batch=256)
+    print("\n[case] inplace 128x64 fp16 tiles", flush=True)
+    n = wl.elements * 2
+    x = make_input(wl.seed, n)
+    ref = np.empty_like(x)
+    oracle.permute(x, ref, 2, wl.extents, wl.src_strides, wl.dst_strides, (0, 0), wl.batch)
+    buf = torch.from_numpy(x).cuda()
+    tpl.permute(buf, buf, wl.extents, wl.src_strides, wl.dst_strides, batch=wl.batch, dtype_bytes=2)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), ref)
+
+
+def test_overlap_other_than_in_place_is_refused():
+    torch = _torch()
+    print("\n[case] partial overlap -> TPL_E_ALIAS, buffer untouched", flush=True)
+    x = make_input(7, 16384 * 4)
+    buf = torch.from_numpy(x).cuda()
+    with pytest.raises(tpl.TplError) as e:
+        # dst starts 64 elements into src
+        tpl.permute(buf, buf, (4, 32), (32, 1), (1, 4), src_offset=0, dst_offset=64, batch=8, dtype_bytes=4)
+    assert e.value.status == tpl.TPL_E_ALIAS
+    # a square in-place transpose over several tiles moves data across units: refused too
+    with pytest.raises(tpl.TplError) as e:
+        tpl.permute(buf, buf, (64, 32), (32, 1), (1, 64), batch=2, dtype_bytes=8)
+    assert e.value.status == tpl.TPL_E_ALIAS
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), x)
+
+
+def test_inplace_single_tile_transpose():
+    """A 64x64 fp32 transpose is one workgroup tile: it may run in place."""
+    torch = _torch()
+    print("\n[case] in-place 64x64 fp32 transpose (one tile)", flush=True)
+    x = make_input(8, 64 * 64 * 4)
+    ref = np.empty_like(x)
+    oracle.permute(x, ref, 4, (64, 64), (64, 1), (1, 64))
+    assert tpl.tpl_plan(4, (64, 64), (64, 1), (1, 64)).kernel == "lds"
+    buf = torch.from_numpy(x).cuda()
+    tpl.permute(buf, buf, (64, 64), (64, 1), (1, 64), dtype_bytes=4)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("w,ext,ss,ds,status", [
+    (3, (4, 32), (32, 1), (1, 4), tpl.TPL_E_DTYPE_WIDTH),
+    (4, (4, 32), (32, 1), (1, 2), tpl.TPL_E_LAYOUT),
+    (4, (4, 32), (32, 1), (0, 4), tpl.TPL_E_LAYOUT),
+])
+def test_declined_call_leaves_dst_untouched(w, ext, ss, ds, status):
+    torch = _torch()
+    print(f"\n[case] decline status {status}", flush=True)
+    s = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    d = torch.full((4096,), SENTINEL, dtype=torch.uint8, device="cuda")
+    st = tpl.tpl_permute(s.data_ptr(), d.data_ptr(), w, ext, ss, ds, (0, 0), 1, 0)
+    assert st == status
+    torch.cuda.synchronize()
+    assert bool((d == SENTINEL).all())
+
+
+def test_empty_launches_nothing():
+    torch = _torch()
+    print("\n[case] empty extents and batch 0", flush=True)
+    s = torch.zeros(512, dtype=torch.uint8, device="cuda")
+    d = torch.full((512,), SENTINEL, dtype=torch.uint8, device="cuda")
+    tpl.permute(d, s, (0, 32), (32, 1), (1, 4), dtype_bytes=4)
+    tpl.permute(d, s, (4, 32), (32, 1), (1, 4), batch=0, dtype_bytes=4)
+    torch.cuda.synchronize()
+    assert bool((d == SENTINEL).all())
+
+
+def test_repeatable():
+    torch = _torch()
+    print("\n[case] the same call twice gives identical bytes", flush=True)
+    wl = workloads.scaled(workloads.TILE_128x64, batch=512)
+    x = torch.from_numpy(make_input(3, wl.elements * 2)).cuda()
+    outs = []
+    for _ in range(2):
+        d = torch.full((wl.elements * 2,), SENTINEL, dtype=torch.uint8, device="cuda")
+        tpl.permute(d, x, wl.extents, wl.src_strides, wl.dst_strides, batch=wl.batch, dtype_bytes=2)
+        outs.append(d)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_big_index_path_sampled():
+    """More than 2^31 elements (64-bit index math): checked on sampled coordinates."""
+    torch = _torch()
+    ext, ss, ds, w = (48, 65536, 704), (704 * 65536, 704, 1), (704 * 65536, 1, 65536), 1
+    n = 48 * 65536 * 704
+    assert n >= 1 << 31
+    plan = tpl.tpl_plan(w, ext, ss, ds)
+    print(f"\n[case] big index path: {n} elements, kernel {plan.kernel}", flush=True)
+    x = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+    d = torch.full((n,), SENTINEL, dtype=torch.uint8, device="cuda")
+    tpl.permute(d, x, ext, ss, ds, dtype_bytes=w)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    coords = np.stack([rng.integers(0, e, 4096) for e in ext], axis=1)
+    src_idx = [oracle.address(tuple(int(v) for v in c), ss) for c in coords]
+    dst_idx = [oracle.address(tuple(int(v) for v in c), ds) for c in coords]
+    xs = x[torch.tensor(src_idx, device="cuda")].cpu().numpy()
+    ys = d[torch.tensor(dst_idx, device="cuda")].cpu().numpy()
+    assert np.array_equal(xs, ys)
+    # every destination byte was written (no sentinel left where the sample says data)
+    assert int((d == SENTINEL).sum()) == int((x == SENTINEL).sum())
