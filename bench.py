@@ -121,16 +121,18 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify):
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # One event at every launch boundary, recorded on the launch stream: the
+    # time between two neighbours is one launch (the queue stays full).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        ev[i][0].record(stream)
+        ev[i].record(stream)
         launch(warmup + i)
-        ev[i][1].record(stream)
+    ev[steps].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    kernel_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     avg_ms = sum(kernel_ms) / len(kernel_ms)
     elapsed = t1 - t0
     value = wl.bytes_moved * steps / elapsed / 1e9
@@ -189,7 +191,7 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="sf_transpose_2^20x4x32_f32")
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
@@ -207,7 +209,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    by_name = {w.name: w for w in workloads.ALL}
+    by_name = {w.name: w for w in workloads.ALL + [workloads.COPY_CALIBRATION]}
     if a.all:
         for wl in workloads.ALL:
             print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify)), flush=True)

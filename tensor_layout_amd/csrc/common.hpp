@@ -103,11 +103,12 @@ struct CopyArgs {
 struct QuadArgs {
     const uint8_t* src;
     uint8_t* dst;
-    int64_t nquads;      // 4x4 blocks overall
-    FastDiv div_qpr;     // 4x4 blocks per batch item (e_a / 4)
-    int64_t qpr;
+    int64_t nunits;      // work units overall (4x32 blocks when wide, else 4x4 blocks)
+    FastDiv div_upr;     // units per batch item
+    int64_t upr;
     int64_t s_b;         // source stride of the 4-row mode (elements)
     int64_t d_a;         // destination stride of the contiguous-source mode (elements)
+    int32_t wide;        // 1: 4x32 blocks, lane-ordered 128-byte row loads
     Modes batch;
 };
 
@@ -138,7 +139,9 @@ struct Reg16Args {
 // Tiled LDS kernel geometry: one workgroup moves one TB x TA tile
 // (TB along the destination-contiguous mode b, TA along the
 // source-contiguous mode a).  NT = tile_bytes / 64 threads, each thread
-// loading four 16-byte chunks.
+// loading four 16-byte chunks.  The read phase gathers, per lane, one
+// 16-byte destination chunk: 4*g dwords (w <= 4, g elements per dword),
+// two 8-byte elements (w = 8) or one 16-byte element (w = 16).
 
 struct LdsShape {
     int w, tb, ta;
@@ -147,8 +150,8 @@ struct LdsShape {
     constexpr TPL_HD int tile_bytes() const { return tb * ta * w; }
     constexpr TPL_HD int threads() const { return tile_bytes() / 64; }
     constexpr TPL_HD int g() const { return w >= 4 ? 1 : 4 / w; }         // elements per dword
-    constexpr TPL_HD int read_bytes() const { return w >= 8 ? 8 : 4; }    // LDS read width
-    constexpr TPL_HD int reads_per_group() const { return w >= 8 ? 2 : 4 * g(); }  // P of the read phase
+    constexpr TPL_HD int read_bytes() const { return w >= 8 ? w : 4; }    // LDS read width
+    constexpr TPL_HD int reads_per_group() const { return w >= 8 ? 16 / w : 4 * g(); }  // P of the read phase
     constexpr TPL_HD int nq() const { return tb * w / 16; }              // 16-byte chunks per destination row
     constexpr TPL_HD int ql() const { return nq() < 8 ? nq() : 8; }      // chunks along b in neighbouring lanes
     constexpr TPL_HD int cols() const { return w >= 8 ? ta : ta * w / 4; } // read columns (dwords, or 8-byte elements)

@@ -24,7 +24,6 @@ namespace tpl {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kQuadUnroll = 2;
 constexpr int64_t kMaxThreads = (int64_t)1 << 31;   // grid * block kept below 2^32
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
@@ -86,67 +85,79 @@ __global__ void __launch_bounds__(256) k_copy(CopyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Quad kernel: fp32 tiles whose destination-contiguous mode has extent 4.
-// A lane quad loads a 4x4 block (lane i: row i, four consecutive columns),
-// transposes it across the quad with two DPP exchange stages, and lane i
-// stores column i (four rows, 16 contiguous bytes).  A wave moves 16 blocks
-// per instruction; for the 4x32 scale-factor tile that is two whole tiles,
-// every 128-byte line of which is read and written by one instruction.
+// Quad kernel: fp32 tiles whose destination-contiguous mode b has extent 4.
+// Each 4x4 block (4 rows of b, 4 consecutive columns of a) sits in four lanes
+// that each hold one row (16 bytes); two exchange stages transpose it so that
+// each lane holds one column, i.e. 16 contiguous destination bytes.  One wave
+// per workgroup, one 16-byte load and store per lane.
+//
+// Wide units (a-extent a multiple of 32): a half-wave takes a 4x32 block,
+// lane l = 8r + q loading row r, columns 4q..4q+3, so each row's 128 bytes
+// are read by eight neighbouring lanes.  The rows of a 4x4 block are then 8
+// and 16 lanes apart: the first stage uses a DPP row rotation by 8 (lanes
+// l^8 inside a 16-lane row), the second a ds_swizzle exchanging l^16.
+// Narrow units: a lane quad takes one 4x4 block (lane i = row i) and both
+// stages are DPP quad permutations.  A stage swaps, between the two lanes,
+// the entries whose column bit differs from the lane's row bit.
 
-__device__ __forceinline__ uint32_t quad_swap1(uint32_t x) {   // lane i reads lane i^1
+__device__ __forceinline__ uint32_t xchg_q1(uint32_t x) {   // quad_perm [1,0,3,2]: lane i^1
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
 }
-__device__ __forceinline__ uint32_t quad_swap2(uint32_t x) {   // lane i reads lane i^2
+__device__ __forceinline__ uint32_t xchg_q2(uint32_t x) {   // quad_perm [2,3,0,1]: lane i^2
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
 }
+__device__ __forceinline__ uint32_t xchg_l8(uint32_t x) {   // row_ror:8: lane l^8 in its 16-lane row
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t xchg_l16(uint32_t x) {  // swizzle, and 0x1f or 0 xor 0x10: lane l^16
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+}
 
-__device__ __forceinline__ u32x4 quad_transpose(u32x4 v, int i) {
-    // Stage 1: lanes i, i^1 swap the entries whose column parity differs
-    // from their row parity.  Stage 2: the same with bit 1 and lanes i^2.
-    const bool odd = i & 1, hi = i & 2;
+template <bool WIDE>
+__device__ __forceinline__ u32x4 transpose4(u32x4 v, int row) {
+    const bool b0 = row & 1, b1 = row & 2;
     uint32_t x0 = v.x, x1 = v.y, x2 = v.z, x3 = v.w;
-    uint32_t u0 = quad_swap1(odd ? x0 : x1);
-    uint32_t u1 = quad_swap1(odd ? x2 : x3);
-    uint32_t a0 = odd ? u0 : x0, a1 = odd ? x1 : u0;
-    uint32_t a2 = odd ? u1 : x2, a3 = odd ? x3 : u1;
-    uint32_t u2 = quad_swap2(hi ? a0 : a2);
-    uint32_t u3 = quad_swap2(hi ? a1 : a3);
+    uint32_t s0 = b0 ? x0 : x1, s1 = b0 ? x2 : x3;
+    uint32_t u0 = WIDE ? xchg_l8(s0) : xchg_q1(s0);
+    uint32_t u1 = WIDE ? xchg_l8(s1) : xchg_q1(s1);
+    uint32_t a0 = b0 ? u0 : x0, a1 = b0 ? x1 : u0;
+    uint32_t a2 = b0 ? u1 : x2, a3 = b0 ? x3 : u1;
+    uint32_t s2 = b1 ? a0 : a2, s3 = b1 ? a1 : a3;
+    uint32_t u2 = WIDE ? xchg_l16(s2) : xchg_q2(s2);
+    uint32_t u3 = WIDE ? xchg_l16(s3) : xchg_q2(s3);
     u32x4 y;
-    y.x = hi ? u2 : a0;
-    y.y = hi ? u3 : a1;
-    y.z = hi ? a2 : u2;
-    y.w = hi ? a3 : u3;
+    y.x = b1 ? u2 : a0;
+    y.y = b1 ? u3 : a1;
+    y.z = b1 ? a2 : u2;
+    y.w = b1 ? a3 : u3;
     return y;
 }
 
-template <int U, bool BIG>
-__global__ void __launch_bounds__(256) k_quad(QuadArgs a) {
-    const int i = threadIdx.x & 3;
-    const int qi = threadIdx.x >> 2;   // 64 quads per workgroup step
-    for (int64_t base = (int64_t)blockIdx.x * U * 64; base < a.nquads; base += (int64_t)gridDim.x * U * 64) {
-        u32x4 v[U];
-        int64_t dofs[U];
-        bool act[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int64_t Q = base + u * 64 + qi;
-            act[u] = Q < a.nquads;
-            v[u] = u32x4{0, 0, 0, 0};
-            dofs[u] = 0;
-            if (act[u]) {
-                int64_t item, qa;
-                split<BIG>(Q, a.qpr, a.div_qpr, item, qa);
-                int64_t so, d_o;
-                modes_offsets<BIG>(a.batch, item, so, d_o);
-                v[u] = ld16(a.src + (so + i * a.s_b + 4 * qa) * 4);
-                dofs[u] = (d_o + (4 * qa + i) * a.d_a) * 4;
-            }
+template <bool WIDE, bool BIG>
+__global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
+    const int lane = threadIdx.x & 63;
+    // WIDE: half-wave h takes unit 2g+h; row r = (lane>>3)&3, column group q = lane&7.
+    // narrow: quad qi takes unit 16g+qi; row r = lane&3.
+    const int r = WIDE ? (lane >> 3) & 3 : lane & 3;
+    const int cq = WIDE ? lane & 7 : 0;
+    const int slot = WIDE ? lane >> 5 : lane >> 2;
+    constexpr int per_wave = WIDE ? 2 : 16;
+    for (int64_t g = blockIdx.x; g * per_wave < a.nunits; g += gridDim.x) {
+        const int64_t U = g * per_wave + slot;
+        const bool act = U < a.nunits;
+        u32x4 v = u32x4{0, 0, 0, 0};
+        int64_t dofs = 0;
+        if (act) {
+            int64_t item, ua;
+            split<BIG>(U, a.upr, a.div_upr, item, ua);
+            int64_t so, d_o;
+            modes_offsets<BIG>(a.batch, item, so, d_o);
+            const int64_t a0 = WIDE ? 32 * ua + 4 * cq : 4 * ua;   // first column this lane loads
+            v = ld16(a.src + (so + r * a.s_b + a0) * 4);
+            dofs = (d_o + (a0 + r) * a.d_a) * 4;                  // after the exchange: column a0 + r
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            u32x4 y = quad_transpose(v[u], i);
-            if (act[u]) st16(a.dst + dofs[u], y);
-        }
+        const u32x4 y = transpose4<WIDE>(v, r);
+        if (act) st16(a.dst + dofs, y);
     }
 }
 
@@ -185,8 +196,7 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
     constexpr LdsShape SH{W, TB, TA};
     constexpr int NT = TB * TA * W / 64;
     constexpr int CPR = TA * W / 16;
-    constexpr int G = (W >= 4) ? 1 : 4 / W;
-    constexpr int R = (W >= 8) ? 2 : 4 * G;          // reads per group
+    constexpr int R = SH.reads_per_group();          // reads per group
     constexpr int GPT = SH.groups() / NT;             // groups per thread
     constexpr int NP = 16 / WW;                       // pieces per chunk
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -198,9 +208,12 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
     const int pitch = a.pitch;
 
     for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        // Consecutive workgroups take consecutive tiles along b: together they
+        // write whole destination rows, which HBM takes better than the
+        // equivalent source-row order.
         int64_t rest, tai, item, tbi;
-        split<BIG>(tile, a.nta, a.div_nta, rest, tai);
-        split<BIG>(rest, a.ntb, a.div_ntb, item, tbi);
+        split<BIG>(tile, a.ntb, a.div_ntb, rest, tbi);
+        split<BIG>(rest, a.nta, a.div_nta, item, tai);
         int64_t so, d_o;
         modes_offsets<BIG>(a.batch, item, so, d_o);
         const int64_t b0 = tbi * TB, a0 = tai * TA;
@@ -213,10 +226,11 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
                 if (bb >= nb || aa >= na) continue;
                 const uint8_t* s = a.src + (so + (b0 + bb) * a.s_b + a0 + aa) * W;
                 uint8_t* d = a.dst + (d_o + (a0 + aa) * a.d_a + b0 + bb) * W;
-                if (W == 1) *d = *s;
-                else if (W == 2) *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
-                else if (W == 4) *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
-                else *reinterpret_cast<uint64_t*>(d) = *reinterpret_cast<const uint64_t*>(s);
+                if constexpr (W == 1) *d = *s;
+                else if constexpr (W == 2) *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
+                else if constexpr (W == 4) *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
+                else if constexpr (W == 8) *reinterpret_cast<uint64_t*>(d) = *reinterpret_cast<const uint64_t*>(s);
+                else *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
             }
             continue;   // uniform across the workgroup
         }
@@ -236,9 +250,9 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
         for (int k = 0; k < 4; ++k) {
             const int cid = t + k * NT;
             uint8_t* row = lds + (cid / CPR) * pitch + (cid % CPR) * 16;
-            if (NP == 1) {
+            if constexpr (NP == 1) {
                 *reinterpret_cast<u32x4*>(row) = v[k];
-            } else if (NP == 2) {
+            } else if constexpr (NP == 2) {
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
                     const int h = r ^ key_w;
@@ -261,8 +275,11 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
         for (int k2 = 0; k2 < GPT; ++k2) {
             int col, q;
             lds_group(SH, t, k2, &col, &q);
-            const uint8_t* base = lds + (q * R) * pitch + col * (W >= 8 ? 8 : 4);
-            if (W >= 8) {
+            const uint8_t* base = lds + (q * R) * pitch + col * SH.read_bytes();
+            if constexpr (W == 16) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(base);
+                st16(dt + (int64_t)col * a.d_a * 16 + q * 16, x);
+            } else if constexpr (W == 8) {
                 uint32_t lo[2], hi[2];
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
@@ -282,9 +299,9 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
                     d[r] = *reinterpret_cast<const uint32_t*>(base + j * pitch);
                 }
                 unrotate<R>(d, key_r);
-                if (W == 4) {
+                if constexpr (W == 4) {
                     st16(dt + (int64_t)col * a.d_a * 4 + q * 16, u32x4{d[0], d[1], d[2], d[3]});
-                } else if (W == 2) {
+                } else if constexpr (W == 2) {
                     // d[m] = (b0+m, a=2col) | (b0+m, a=2col+1) << 16
                     u32x4 o0, o1;
                     uint32_t* p0 = reinterpret_cast<uint32_t*>(&o0);
@@ -365,12 +382,15 @@ static hipError_t launch_lds(const Plan& p, hipStream_t st) {
 #define TPL_LDS_SHAPE(W_, TB_, TA_) TPL_LDS_CASE(W_, TB_, TA_, 16) TPL_LDS_CASE(W_, TB_, TA_, 8) TPL_LDS_CASE(W_, TB_, TA_, 4)
     TPL_LDS_SHAPE(1, 128, 128)
     TPL_LDS_SHAPE(1, 64, 128)
+    TPL_LDS_SHAPE(2, 256, 64)
     TPL_LDS_SHAPE(2, 128, 64)
     TPL_LDS_SHAPE(2, 32, 64)
     TPL_LDS_SHAPE(4, 64, 64)
     TPL_LDS_SHAPE(4, 32, 32)
     TPL_LDS_SHAPE(8, 32, 64)
     TPL_LDS_SHAPE(8, 16, 32)
+    TPL_LDS_SHAPE(16, 16, 64)
+    TPL_LDS_SHAPE(16, 16, 16)
 #undef TPL_LDS_SHAPE
 #undef TPL_LDS_CASE
     return hipErrorInvalidConfiguration;
@@ -404,8 +424,9 @@ static hipError_t launch_big(const Plan& p, const uint8_t* src, uint8_t* dst, hi
         QuadArgs a = p.quad;
         a.src = src;
         a.dst = dst;
-        int64_t grid = (a.nquads + 64 * kQuadUnroll - 1) / (64 * kQuadUnroll);
-        hipLaunchKernelGGL((k_quad<kQuadUnroll, BIG>), dim3((unsigned)cap_grid(grid, 256)), dim3(256), 0, st, a);
+        dim3 grid((unsigned)cap_grid(p.grid, 64)), block(64);
+        if (a.wide) hipLaunchKernelGGL((k_quad<true, BIG>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_quad<false, BIG>), grid, block, 0, st, a);
         return hipGetLastError();
     }
     case TPL_KERNEL_LDS: {
@@ -613,8 +634,6 @@ int tpl_plan(int dtype_bytes, int rank, const int64_t* extents, const int64_t* s
             static const int64_t zero[2] = {0, 0};
             p = tpl::plan_gfx950(dtype_bytes, rank, extents, src_strides, dst_strides,
                                  elem_offsets ? elem_offsets : zero, batch, 256, 256);
-            if (p.kernel == TPL_KERNEL_QUAD && p.status == TPL_OK)
-                p.grid = (p.quad.nquads + 64 * tpl::kQuadUnroll - 1) / (64 * tpl::kQuadUnroll);
         } else {
             p.status = TPL_E_ARG;
             p.reason = "unknown geometry";

@@ -306,9 +306,10 @@ static LdsChoice choose_lds(const LdsShape& sh) {
 // Tile shapes the library instantiates: (w, TB, TA), largest first.
 static const LdsShape kLdsShapes[] = {
     {1, 128, 128}, {1, 64, 128},
-    {2, 128, 64}, {2, 32, 64},
+    {2, 256, 64}, {2, 128, 64}, {2, 32, 64},
     {4, 64, 64}, {4, 32, 32},
     {8, 32, 64}, {8, 16, 32},
+    {16, 16, 64}, {16, 16, 16},
 };
 
 const LdsShape* lds_shapes(int* n) {
@@ -457,8 +458,10 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
         if (p.big) p.grid = std::min<int64_t>(p.grid, 1 << 15);
     };
 
-    // 16-byte elements: one element is one dwordx4; lanes form 8x8 blocks.
-    if (w == 16 && a >= 0 && b >= 0 && a != b && sa % 16 == 0 && da % 16 == 0) {
+    // 16-byte elements too small for an LDS tile: one element is one dwordx4;
+    // lanes form 8x8 blocks.
+    if (w == 16 && a >= 0 && b >= 0 && a != b && sa % 16 == 0 && da % 16 == 0 &&
+        (sh.m[b].e < 16 || sh.m[a].e < 16)) {
         p.kernel = TPL_KERNEL_REG16;
         Reg16Args& r = p.reg16;
         r.e_b = sh.m[b].e;
@@ -505,7 +508,7 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
         return p;
     }
 
-    if (a >= 0 && b >= 0 && w <= 8) {
+    if (a >= 0 && b >= 0) {
         const Mode& ma = sh.m[a];
         const Mode& mb = sh.m[b];
         bool src_ok = sa % 16 == 0 && all_aligned(sh, a, -1, w, true, 16);
@@ -514,24 +517,27 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
         if (w == 4 && mb.e == 4 && ma.e % 4 == 0 && src_ok && dst_ok) {
             p.kernel = TPL_KERNEL_QUAD;
             QuadArgs& q = p.quad;
-            q.qpr = ma.e / 4;
-            q.div_qpr = make_fastdiv((uint32_t)std::min<int64_t>(q.qpr, 0x7fffffff));
+            // Wide units (4 rows x 32 columns, one per 32-lane half-wave) when the
+            // rows allow it: each row's 128 bytes are then one lane-ordered load.
+            q.wide = (ma.e % 32 == 0) ? 1 : 0;
+            q.upr = q.wide ? ma.e / 32 : ma.e / 4;
+            q.div_upr = make_fastdiv((uint32_t)std::min<int64_t>(q.upr, 0x7fffffff));
             q.s_b = mb.s;
             q.d_a = ma.d;
             int64_t items = 1;
             for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
-            q.nquads = items * q.qpr;
-            if (q.nquads >= ((int64_t)1 << 31)) p.big = true;
+            q.nunits = items * q.upr;
+            if (q.nunits >= ((int64_t)1 << 31)) p.big = true;
             set_modes(q.batch, sh, others, no);
             p.P = 4;
             p.tile_b = 4;
-            p.tile_a = (int)std::min<int64_t>(ma.e, 64);
-            p.block = 256;
-            // One quad block per lane quad; 64 quad blocks per workgroup per step.
-            p.grid = 0;  // set at launch (depends on the unroll)
-            // Each batch item is moved by one wave-instruction when its 4x4
-            // blocks fit one wave (16 quads) and tile the wave evenly.
-            p.unit_is_item = (q.qpr <= 16 && 16 % q.qpr == 0);
+            p.tile_a = q.wide ? 32 : 4;
+            p.block = 64;   // one wave per workgroup
+            const int64_t per_wave = q.wide ? 2 : 16;
+            p.grid = (q.nunits + per_wave - 1) / per_wave;
+            // One wave-instruction moves each batch item (all its loads complete
+            // before its stores) when the item's units tile the wave evenly.
+            p.unit_is_item = q.wide ? (q.upr <= 2) : (q.upr <= 16 && 16 % q.upr == 0);
             return p;
         }
         // Tiled LDS transpose.

@@ -147,7 +147,7 @@ EXPECTED_KERNEL = {
     "axes0231_64x128x32x32_w4": "lds",
     "axes0231_64x128x32x32_w8": "lds",
     "transpose_16384x16384_bf16": "lds",
-    "transpose_4096x4096_16B": "reg16",
+    "transpose_4096x4096_16B": "lds",
 }
 
 
@@ -196,9 +196,9 @@ def tile_programs(w, tb, ta, pitch, ww, shift_w, mask_w, shift_r, mask_r):
                 yield True, ww, addrs
     nq = tb * w // 16
     ql = min(8, nq)
-    cols = ta if w == 8 else ta * w // 4
-    reads = 2 if w == 8 else 4 * (4 // w if w < 4 else 1)
-    rb = 8 if w == 8 else 4
+    cols = ta if w >= 8 else ta * w // 4
+    reads = 16 // w if w >= 8 else 4 * (4 // w if w < 4 else 1)
+    rb = w if w >= 8 else 4
     gpt = cols * nq // threads
     for wave in range(threads // 64):
         for slot in range(gpt):
@@ -213,10 +213,21 @@ def tile_programs(w, tb, ta, pitch, ww, shift_w, mask_w, shift_r, mask_r):
                 yield False, rb, addrs
 
 
-@pytest.mark.parametrize("w", [1, 2, 4, 8])
-def test_lds_choice_is_conflict_free(w):
-    wl = workloads.mixed_width(w)
-    p = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides)
+LDS_CASES = [workloads.mixed_width(w) for w in (1, 2, 4, 8)] + [
+    workloads.TILE_128x64, workloads.BF16_16K, workloads.W16_4K,
+    workloads.Workload("w16_small", 16, (40, 40), (40, 1), (1, 40)),
+    workloads.Workload("w1_small", 1, (80, 144), (160, 1), (1, 96)),
+    workloads.Workload("w2_small", 2, (96, 160), (168, 1), (1, 104)),
+    workloads.Workload("w4_small", 4, (40, 40), (40, 1), (1, 40)),
+    workloads.Workload("w8_small", 8, (24, 40), (40, 1), (1, 24)),
+]
+
+
+@pytest.mark.parametrize("wl", LDS_CASES, ids=lambda w: w.name)
+def test_lds_choice_is_conflict_free(wl):
+    w = wl.w
+    p = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, batch=wl.batch)
+    assert p.kernel == "lds", p
     tb, ta = p.tile
     ww = 16 if p.lds_pitch % 16 == 0 else 8 if p.lds_pitch % 8 == 0 else 4
     progs = list(tile_programs(w, tb, ta, p.lds_pitch, ww, p.shift_w, p.mask_w, p.shift, p.mask))

@@ -114,6 +114,8 @@ RAGGED = [
     ("lds_w2_small_tile", 2, (96, 160), (168, 1), (1, 104), "lds"),
     ("lds_w1_small_tile", 1, (80, 144), (160, 1), (1, 96), "lds"),
     ("reg16_ragged", 16, (13, 27), (27, 1), (1, 13), "reg16"),
+    ("lds_w16_ragged", 16, (3, 40, 70), (40 * 70, 70, 1), (70 * 40, 1, 40), "lds"),
+    ("lds_w16_big_tile_ragged", 16, (50, 200), (200, 1), (1, 50), "lds"),
     ("quad_qpr9", 4, (4, 36), (36, 1), (1, 4), "quad"),
     ("quad_padded", 4, (5, 4, 32), (160, 40, 1), (256, 1, 8), "quad"),
     ("copy_outer_perm", 4, (8, 64, 32), (32, 256, 1), (2048, 32, 1), "copy"),
