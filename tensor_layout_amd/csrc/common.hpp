@@ -17,7 +17,7 @@
 namespace tpl {
 
 constexpr int kMaxShard = 10;   // shard modes (8 user modes + batch + slack)
-constexpr int kMaxBatch = 8;    // modes a kernel decomposes as "batch"
+constexpr int kMaxBatch = 10;   // modes a kernel decomposes (at most the whole shard)
 constexpr int kWave = 64;       // gfx950 wavefront
 
 // Division by an invariant 31-bit integer with a multiply and a shift
@@ -59,24 +59,37 @@ struct Modes {
 };
 
 template <bool BIG>
+TPL_HD void modes_step(const Modes& m, int i, int64_t& idx, int64_t& so, int64_t& d_o) {
+    int64_t q, r;
+    if (BIG) {
+        q = idx / m.ext[i];
+        r = idx - q * m.ext[i];
+    } else {
+        uint32_t qq = fdiv((uint32_t)idx, m.div[i]);
+        r = (int64_t)((uint32_t)idx - qq * m.div[i].d);
+        q = qq;
+    }
+    so += r * m.ss[i];
+    d_o += r * m.ds[i];
+    idx = q;
+}
+
+// NB >= 0: the kernel was built for exactly NB modes, so the loop unrolls and
+// the mode table is read once; NB < 0: m.n modes, decided at run time.
+template <int NB, bool BIG>
 TPL_HD void modes_offsets(const Modes& m, int64_t idx, int64_t& so, int64_t& d_o) {
     so = 0;
     d_o = 0;
-    for (int i = m.n - 1; i >= 0; --i) {
-        int64_t q, r;
-        if (BIG) {
-            q = idx / m.ext[i];
-            r = idx - q * m.ext[i];
-        } else {
-            uint32_t qq = fdiv((uint32_t)idx, m.div[i]);
-            r = (int64_t)((uint32_t)idx - qq * m.div[i].d);
-            q = qq;
-        }
-        so += r * m.ss[i];
-        d_o += r * m.ds[i];
-        idx = q;
+    if constexpr (NB >= 0) {
+#pragma unroll
+        for (int i = NB - 1; i >= 0; --i) modes_step<BIG>(m, i, idx, so, d_o);
+    } else {
+        for (int i = m.n - 1; i >= 0; --i) modes_step<BIG>(m, i, idx, so, d_o);
     }
 }
+
+// Kernels are built for 0, 1 and 2 batch modes and for any count.
+inline int nb_class(int n) { return n <= 2 ? n : -1; }
 
 // ---------------------------------------------------------------------------
 // Kernel argument blocks (passed by value).

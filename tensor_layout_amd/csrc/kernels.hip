@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(256) k_gather(GatherArgs a) {
     const int nu = a.w / Unit<T>::bytes;
     for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < a.total; n += stride) {
         int64_t so, d_o;
-        modes_offsets<BIG>(a.modes, n, so, d_o);
+        modes_offsets<-1, BIG>(a.modes, n, so, d_o);
         const T* s = reinterpret_cast<const T*>(a.src + so * a.w);
         T* d = reinterpret_cast<T*>(a.dst + d_o * a.w);
         for (int u = 0; u < nu; ++u) d[u] = s[u];
@@ -72,14 +72,14 @@ __global__ void __launch_bounds__(256) k_gather(GatherArgs a) {
 // ---------------------------------------------------------------------------
 // Copy: both sides contiguous along one mode; 16-byte chunks of the runs.
 
-template <bool BIG>
+template <int NB, bool BIG>
 __global__ void __launch_bounds__(256) k_copy(CopyArgs a) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < a.nchunks; id += stride) {
         int64_t row, c;
         split<BIG>(id, a.cpr, a.div_cpr, row, c);
         int64_t so, d_o;
-        modes_offsets<BIG>(a.rows, row, so, d_o);
+        modes_offsets<NB, BIG>(a.rows, row, so, d_o);
         st16(a.dst + d_o * a.w + c * 16, ld16(a.src + so * a.w + c * 16));
     }
 }
@@ -95,7 +95,8 @@ __global__ void __launch_bounds__(256) k_copy(CopyArgs a) {
 // lane l = 8r + q loading row r, columns 4q..4q+3, so each row's 128 bytes
 // are read by eight neighbouring lanes.  The rows of a 4x4 block are then 8
 // and 16 lanes apart: the first stage uses a DPP row rotation by 8 (lanes
-// l^8 inside a 16-lane row), the second a ds_swizzle exchanging l^16.
+// l^8 inside a 16-lane row), the second v_permlane16_swap (lanes l^16);
+// both are VALU operations, so the kernel issues no LDS instruction at all.
 // Narrow units: a lane quad takes one 4x4 block (lane i = row i) and both
 // stages are DPP quad permutations.  A stage swaps, between the two lanes,
 // the entries whose column bit differs from the lane's row bit.
@@ -109,12 +110,16 @@ __device__ __forceinline__ uint32_t xchg_q2(uint32_t x) {   // quad_perm [2,3,0,
 __device__ __forceinline__ uint32_t xchg_l8(uint32_t x) {   // row_ror:8: lane l^8 in its 16-lane row
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
 }
-__device__ __forceinline__ uint32_t xchg_l16(uint32_t x) {  // swizzle, and 0x1f or 0 xor 0x10: lane l^16
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+__device__ __forceinline__ uint32_t xchg_l16(uint32_t x, int lane) {  // lane l^16
+    // v_permlane16_swap(x, x) swaps the odd 16-lane rows of its first operand
+    // with the even rows of its second: the second result holds x[l+16] in
+    // even rows, the first holds x[l-16] in odd rows.
+    auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
 }
 
 template <bool WIDE>
-__device__ __forceinline__ u32x4 transpose4(u32x4 v, int row) {
+__device__ __forceinline__ u32x4 transpose4(u32x4 v, int row, int lane) {
     const bool b0 = row & 1, b1 = row & 2;
     uint32_t x0 = v.x, x1 = v.y, x2 = v.z, x3 = v.w;
     uint32_t s0 = b0 ? x0 : x1, s1 = b0 ? x2 : x3;
@@ -123,8 +128,8 @@ __device__ __forceinline__ u32x4 transpose4(u32x4 v, int row) {
     uint32_t a0 = b0 ? u0 : x0, a1 = b0 ? x1 : u0;
     uint32_t a2 = b0 ? u1 : x2, a3 = b0 ? x3 : u1;
     uint32_t s2 = b1 ? a0 : a2, s3 = b1 ? a1 : a3;
-    uint32_t u2 = WIDE ? xchg_l16(s2) : xchg_q2(s2);
-    uint32_t u3 = WIDE ? xchg_l16(s3) : xchg_q2(s3);
+    uint32_t u2 = WIDE ? xchg_l16(s2, lane) : xchg_q2(s2);
+    uint32_t u3 = WIDE ? xchg_l16(s3, lane) : xchg_q2(s3);
     u32x4 y;
     y.x = b1 ? u2 : a0;
     y.y = b1 ? u3 : a1;
@@ -133,7 +138,7 @@ __device__ __forceinline__ u32x4 transpose4(u32x4 v, int row) {
     return y;
 }
 
-template <bool WIDE, bool BIG>
+template <bool WIDE, int NB, bool BIG>
 __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
     const int lane = threadIdx.x & 63;
     // WIDE: half-wave h takes unit 2g+h; row r = (lane>>3)&3, column group q = lane&7.
@@ -151,12 +156,12 @@ __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
             int64_t item, ua;
             split<BIG>(U, a.upr, a.div_upr, item, ua);
             int64_t so, d_o;
-            modes_offsets<BIG>(a.batch, item, so, d_o);
+            modes_offsets<NB, BIG>(a.batch, item, so, d_o);
             const int64_t a0 = WIDE ? 32 * ua + 4 * cq : 4 * ua;   // first column this lane loads
             v = ld16(a.src + (so + r * a.s_b + a0) * 4);
             dofs = (d_o + (a0 + r) * a.d_a) * 4;                  // after the exchange: column a0 + r
         }
-        const u32x4 y = transpose4<WIDE>(v, r);
+        const u32x4 y = transpose4<WIDE>(v, r, lane);
         if (act) st16(a.dst + dofs, y);
     }
 }
@@ -191,7 +196,7 @@ __device__ __forceinline__ void unrotate(uint32_t (&d)[N], int key) {
     }
 }
 
-template <int W, int TB, int TA, int WW, bool BIG>
+template <int W, int TB, int TA, int WW, int NB, bool BIG>
 __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
     constexpr LdsShape SH{W, TB, TA};
     constexpr int NT = TB * TA * W / 64;
@@ -215,7 +220,7 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
         split<BIG>(tile, a.ntb, a.div_ntb, rest, tbi);
         split<BIG>(rest, a.nta, a.div_nta, item, tai);
         int64_t so, d_o;
-        modes_offsets<BIG>(a.batch, item, so, d_o);
+        modes_offsets<NB, BIG>(a.batch, item, so, d_o);
         const int64_t b0 = tbi * TB, a0 = tai * TA;
 
         if (b0 + TB > a.e_b || a0 + TA > a.e_a) {
@@ -344,7 +349,7 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
 // stores it at destination row a0+j, element b0+i (eight lanes per 128-byte
 // destination line).  An element is one dwordx4, so no exchange is needed.
 
-template <bool BIG>
+template <int NB, bool BIG>
 __global__ void __launch_bounds__(256) k_reg16(Reg16Args a) {
     const int lane = threadIdx.x & 63;
     const int i = lane >> 3, j = lane & 7;
@@ -354,7 +359,7 @@ __global__ void __launch_bounds__(256) k_reg16(Reg16Args a) {
         split<BIG>(blk, a.nba, a.div_nba, rest, tai);
         split<BIG>(rest, a.nbb, a.div_nbb, item, tbi);
         int64_t so, d_o;
-        modes_offsets<BIG>(a.batch, item, so, d_o);
+        modes_offsets<NB, BIG>(a.batch, item, so, d_o);
         const int64_t bb = tbi * 8 + i, aa = tai * 8 + j;
         if (bb < a.e_b && aa < a.e_a)
             st16(a.dst + (d_o + aa * a.d_a + bb) * 16, ld16(a.src + (so + bb * a.s_b + aa) * 16));
@@ -369,15 +374,14 @@ static int64_t cap_grid(int64_t grid, int64_t block) {
     return grid < lim ? (grid < 1 ? 1 : grid) : lim;
 }
 
-template <bool BIG>
-static hipError_t launch_lds(const Plan& p, hipStream_t st) {
+template <int NB, bool BIG>
+static hipError_t launch_lds(const Plan& p, const LdsArgs& a, hipStream_t st) {
     dim3 grid((unsigned)cap_grid(p.grid, p.block)), block((unsigned)p.block);
-    const LdsArgs& a = p.lds;
     const int w = p.w, tb = p.tile_b, ta = p.tile_a, ww = p.ww;
-#define TPL_LDS_CASE(W_, TB_, TA_, WW_)                                                         \
-    if (w == W_ && tb == TB_ && ta == TA_ && ww == WW_) {                                        \
-        hipLaunchKernelGGL((k_lds<W_, TB_, TA_, WW_, BIG>), grid, block, p.lds_bytes, st, a);   \
-        return hipGetLastError();                                                                \
+#define TPL_LDS_CASE(W_, TB_, TA_, WW_)                                                             \
+    if (w == W_ && tb == TB_ && ta == TA_ && ww == WW_) {                                            \
+        hipLaunchKernelGGL((k_lds<W_, TB_, TA_, WW_, NB, BIG>), grid, block, p.lds_bytes, st, a);   \
+        return hipGetLastError();                                                                    \
     }
 #define TPL_LDS_SHAPE(W_, TB_, TA_) TPL_LDS_CASE(W_, TB_, TA_, 16) TPL_LDS_CASE(W_, TB_, TA_, 8) TPL_LDS_CASE(W_, TB_, TA_, 4)
     TPL_LDS_SHAPE(1, 128, 128)
@@ -396,10 +400,46 @@ static hipError_t launch_lds(const Plan& p, hipStream_t st) {
     return hipErrorInvalidConfiguration;
 }
 
+template <int NB, bool BIG>
+static hipError_t launch_nb(const Plan& p, const uint8_t* src, uint8_t* dst, hipStream_t st) {
+    switch (p.kernel) {
+    case TPL_KERNEL_COPY: {
+        CopyArgs a = p.copy;
+        a.src = src;
+        a.dst = dst;
+        hipLaunchKernelGGL((k_copy<NB, BIG>), dim3((unsigned)cap_grid(p.grid, 256)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    case TPL_KERNEL_QUAD: {
+        QuadArgs a = p.quad;
+        a.src = src;
+        a.dst = dst;
+        dim3 grid((unsigned)cap_grid(p.grid, 64)), block(64);
+        if (a.wide) hipLaunchKernelGGL((k_quad<true, NB, BIG>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_quad<false, NB, BIG>), grid, block, 0, st, a);
+        return hipGetLastError();
+    }
+    case TPL_KERNEL_LDS: {
+        LdsArgs a = p.lds;
+        a.src = src;
+        a.dst = dst;
+        return launch_lds<NB, BIG>(p, a, st);
+    }
+    case TPL_KERNEL_REG16: {
+        Reg16Args a = p.reg16;
+        a.src = src;
+        a.dst = dst;
+        hipLaunchKernelGGL((k_reg16<NB, BIG>), dim3((unsigned)cap_grid(p.grid, 256)), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+    default:
+        return hipSuccess;
+    }
+}
+
 template <bool BIG>
 static hipError_t launch_big(const Plan& p, const uint8_t* src, uint8_t* dst, hipStream_t st) {
-    switch (p.kernel) {
-    case TPL_KERNEL_GATHER: {
+    if (p.kernel == TPL_KERNEL_GATHER) {
         GatherArgs a = p.gather;
         a.src = src;
         a.dst = dst;
@@ -413,37 +453,11 @@ static hipError_t launch_big(const Plan& p, const uint8_t* src, uint8_t* dst, hi
         }
         return hipGetLastError();
     }
-    case TPL_KERNEL_COPY: {
-        CopyArgs a = p.copy;
-        a.src = src;
-        a.dst = dst;
-        hipLaunchKernelGGL((k_copy<BIG>), dim3((unsigned)cap_grid(p.grid, 256)), dim3(256), 0, st, a);
-        return hipGetLastError();
-    }
-    case TPL_KERNEL_QUAD: {
-        QuadArgs a = p.quad;
-        a.src = src;
-        a.dst = dst;
-        dim3 grid((unsigned)cap_grid(p.grid, 64)), block(64);
-        if (a.wide) hipLaunchKernelGGL((k_quad<true, BIG>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_quad<false, BIG>), grid, block, 0, st, a);
-        return hipGetLastError();
-    }
-    case TPL_KERNEL_LDS: {
-        Plan q = p;
-        q.lds.src = src;
-        q.lds.dst = dst;
-        return launch_lds<BIG>(q, st);
-    }
-    case TPL_KERNEL_REG16: {
-        Reg16Args a = p.reg16;
-        a.src = src;
-        a.dst = dst;
-        hipLaunchKernelGGL((k_reg16<BIG>), dim3((unsigned)cap_grid(p.grid, 256)), dim3(256), 0, st, a);
-        return hipGetLastError();
-    }
-    default:
-        return hipSuccess;
+    switch (nb_class(p.batch_modes)) {
+    case 0: return launch_nb<0, BIG>(p, src, dst, st);
+    case 1: return launch_nb<1, BIG>(p, src, dst, st);
+    case 2: return launch_nb<2, BIG>(p, src, dst, st);
+    default: return launch_nb<-1, BIG>(p, src, dst, st);
     }
 }
 

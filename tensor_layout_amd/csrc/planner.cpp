@@ -139,6 +139,8 @@ static int64_t shard_elements(const Shard& sh) {
 }
 
 static bool set_modes(Modes& out, const Shard& sh, const int* idx, int n) {
+    // n never exceeds the shard rank, which make_shard keeps <= kMaxShard.
+    static_assert(kMaxBatch >= kMaxShard, "mode table must hold a whole shard");
     if (n > kMaxBatch) return false;
     out.n = n;
     for (int i = 0; i < n; ++i) {
@@ -440,6 +442,7 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
     int no = 0;
     for (int i = 0; i < sh.rank; ++i)
         if (i != a && i != b) others[no++] = i;
+    p.batch_modes = no;
 
     auto choose_gather = [&]() {
         p.kernel = TPL_KERNEL_GATHER;

@@ -53,6 +53,7 @@ struct Plan {
     bool big = false;       // 64-bit index math needed
     bool unit_is_item = false;  // each batch item is moved by one work unit (reads before writes)
     int mode_a = -1, mode_b = -1;          // shard indices of the two contiguous modes
+    int batch_modes = 0;                   // modes the kernel decomposes as batch
     int64_t src_off_bytes = 0, dst_off_bytes = 0;
     // kernel arguments (pointers filled at launch)
     GatherArgs gather{};
