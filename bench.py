@@ -191,10 +191,12 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="sf_transpose_2^20x4x32_f32")
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--with-calibration", action="store_true",
+                    help="with --all: also run the 512 MiB identity copy used to scale HBM counters")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-verify", action="store_true")
     a = ap.parse_args()
@@ -211,7 +213,8 @@ def main():
         sys.exit(1)
     by_name = {w.name: w for w in workloads.ALL + [workloads.COPY_CALIBRATION]}
     if a.all:
-        for wl in workloads.ALL:
+        todo = workloads.ALL + ([workloads.COPY_CALIBRATION] if a.with_calibration else [])
+        for wl in todo:
             print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify)), flush=True)
         return
     wl = by_name[a.workload]

@@ -162,22 +162,46 @@ def test_gfx950_kernel_choice(wl):
 # Independent statement of the tiled kernel's LDS access programs and of the
 # measured gfx950 bank model, to check the planner's pitch / XOR choice.
 
-# (is_write, bytes) -> (banks, lanes per pass); sub-dword modelled as b32
+# (is_write, bytes) -> (banks, lanes per pass); sub-dword modelled as b32.
+# ds_read_b128 groups its 16-lane passes by lane bit 5 and the parity of
+# lane bits 2..4 (measured two lanes at a time); the others run consecutive lanes.
 MEASURED = {(False, 4): (32, 32), (False, 8): (64, 32), (False, 16): (64, 16),
             (True, 4): (32, 32), (True, 8): (32, 16), (True, 16): (32, 8)}
 
 
-def conflict_free(addrs, is_write, nbytes):
+def pass_groups(is_write, nbytes):
     banks, per_pass = MEASURED[(is_write, max(4, nbytes))]
-    for p0 in range(0, 64, per_pass):
+    if (is_write, max(4, nbytes)) == (False, 16):
+        groups = {}
+        for lane in range(64):
+            key = (lane >> 5 & 1, bin(lane >> 2 & 7).count("1") & 1)
+            groups.setdefault(key, []).append(lane)
+        return banks, list(groups.values())
+    return banks, [list(range(p0, p0 + per_pass)) for p0 in range(0, 64, per_pass)]
+
+
+def conflict_free(addrs, is_write, nbytes):
+    banks, groups = pass_groups(is_write, nbytes)
+    for lanes in groups:
         used = {}
-        for a in addrs[p0:p0 + per_pass]:
+        for lane in lanes:
+            a = addrs[lane]
             for wd in range(a // 4, a // 4 + max(1, nbytes // 4)):
                 b = wd % banks
                 if b in used and used[b] != wd:
                     return False
                 used[b] = wd
     return True
+
+
+def test_bank_model_reproduces_measured_tile_maps():
+    """Whole-wave ds_read_b128 measurements: a lane reads row L%8 at `pitch`,
+    column L//8 (16 bytes).  Conflict cycles per access measured on MI355X:
+    zero only at pitch 1088 and 320 among those tried."""
+    measured_zero = {1088, 320}
+    for pitch in (1024, 1040, 1056, 1072, 1088, 1104, 1120, 1136, 1152, 1280, 272, 288, 304, 320):
+        addrs = [(lane % 8) * pitch + (lane // 8) * 16 for lane in range(64)]
+        assert conflict_free(addrs, False, 16) == (pitch in measured_zero), pitch
 
 
 def tile_programs(w, tb, ta, pitch, ww, shift_w, mask_w, shift_r, mask_r):
