@@ -22,9 +22,11 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+PROBE = os.path.join(HERE, "lds_probe")
+PROBE_FLAGS = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,7 +37,16 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode})")
     if verbose and msgs:
         print("\n".join(msgs))
+
+
+def build(verbose: bool = False) -> str:
+    """Build libtpl.so and the LDS bank-geometry probe (both in-tree)."""
+    tmp = LIB + ".tmp"
+    _run([HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
+    ptmp = PROBE + ".tmp"
+    _run([HIPCC] + PROBE_FLAGS + [os.path.join(CSRC, "lds_probe.hip"), "-o", ptmp], verbose)
+    os.replace(ptmp, PROBE)
     return LIB
 
 
