@@ -213,12 +213,16 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
     const int pitch = a.pitch;
 
     for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
-        // Consecutive workgroups take consecutive tiles along b: together they
-        // write whole destination rows, which HBM takes better than the
-        // equivalent source-row order.
-        int64_t rest, tai, item, tbi;
+        // Tile order: b fastest, so that neighbouring workgroups write
+        // neighbouring pieces of the same destination rows; and diagonal in
+        // a (the a-tile index is shifted by the b-tile index), so that
+        // neighbouring workgroups read source rows at different column
+        // offsets.  With power-of-two row pitches the plain order sends every
+        // concurrent read of a column band to the same HBM channels.
+        int64_t rest, tq, item, tbi, tai, wrap;
         split<BIG>(tile, a.ntb, a.div_ntb, rest, tbi);
-        split<BIG>(rest, a.nta, a.div_nta, item, tai);
+        split<BIG>(rest, a.nta, a.div_nta, item, tq);
+        split<BIG>(tq + tbi, a.nta, a.div_nta, wrap, tai);
         int64_t so, d_o;
         modes_offsets<NB, BIG>(a.batch, item, so, d_o);
         const int64_t b0 = tbi * TB, a0 = tai * TA;
@@ -393,6 +397,7 @@ static hipError_t launch_lds(const Plan& p, const LdsArgs& a, hipStream_t st) {
     TPL_LDS_SHAPE(4, 32, 32)
     TPL_LDS_SHAPE(8, 32, 64)
     TPL_LDS_SHAPE(8, 16, 32)
+    TPL_LDS_SHAPE(16, 128, 8)
     TPL_LDS_SHAPE(16, 16, 64)
     TPL_LDS_SHAPE(16, 16, 16)
 #undef TPL_LDS_SHAPE

@@ -321,7 +321,7 @@ static const LdsShape kLdsShapes[] = {
     {2, 256, 64}, {2, 128, 64}, {2, 32, 64},
     {4, 64, 64}, {4, 32, 32},
     {8, 32, 64}, {8, 16, 32},
-    {16, 16, 64}, {16, 16, 16},
+    {16, 128, 8}, {16, 16, 64}, {16, 16, 16},
 };
 
 const LdsShape* lds_shapes(int* n) {
