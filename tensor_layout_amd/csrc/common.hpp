@@ -151,17 +151,17 @@ struct Reg16Args {
 // ---------------------------------------------------------------------------
 // Tiled LDS kernel geometry: one workgroup moves one TB x TA tile
 // (TB along the destination-contiguous mode b, TA along the
-// source-contiguous mode a).  NT = tile_bytes / 64 threads, each thread
-// loading four 16-byte chunks.  The read phase gathers, per lane, one
+// source-contiguous mode a).  NT = tile_bytes / (16 * cpt) threads, each
+// thread loading cpt 16-byte chunks.  The read phase gathers, per lane, one
 // 16-byte destination chunk: 4*g dwords (w <= 4, g elements per dword),
 // two 8-byte elements (w = 8) or one 16-byte element (w = 16).
 
 struct LdsShape {
-    int w, tb, ta;
+    int w, tb, ta, cpt;
     constexpr TPL_HD int row_bytes() const { return ta * w; }            // one source row in the tile
     constexpr TPL_HD int chunks_per_row() const { return ta * w / 16; }
     constexpr TPL_HD int tile_bytes() const { return tb * ta * w; }
-    constexpr TPL_HD int threads() const { return tile_bytes() / 64; }
+    constexpr TPL_HD int threads() const { return tile_bytes() / (16 * cpt); }
     constexpr TPL_HD int g() const { return w >= 4 ? 1 : 4 / w; }         // elements per dword
     constexpr TPL_HD int read_bytes() const { return w >= 8 ? w : 4; }    // LDS read width
     constexpr TPL_HD int reads_per_group() const { return w >= 8 ? 16 / w : 4 * g(); }  // P of the read phase
@@ -169,7 +169,7 @@ struct LdsShape {
     constexpr TPL_HD int ql() const { return nq() < 8 ? nq() : 8; }      // chunks along b in neighbouring lanes
     constexpr TPL_HD int cols() const { return w >= 8 ? ta : ta * w / 4; } // read columns (dwords, or 8-byte elements)
     constexpr TPL_HD int groups() const { return cols() * nq(); }
-    constexpr TPL_HD int groups_per_thread() const { return groups() / threads(); }
+    constexpr TPL_HD int groups_per_thread() const { return (groups() + threads() - 1) / threads(); }
 };
 
 // Write phase: thread t, chunk slot k (0..3), piece step r of the chunk.
@@ -197,8 +197,10 @@ TPL_HD void lds_group(const LdsShape& sh, int t, int k2, int* col, int* q) {
     *q = (rest / sh.cols()) * ql + seg;
 }
 
+// Returns -1 when slot k2 of thread t holds no group (the last slot may be partial).
 TPL_HD int lds_read_addr(const LdsShape& sh, int pitch, int t, int k2, int r,
                          int shift_r, int mask_r, int* row_step) {
+    if (t + k2 * sh.threads() >= sh.groups()) return -1;
     int col, q;
     lds_group(sh, t, k2, &col, &q);
     int lane = t & (kWave - 1);

@@ -196,13 +196,13 @@ __device__ __forceinline__ void unrotate(uint32_t (&d)[N], int key) {
     }
 }
 
-template <int W, int TB, int TA, int WW, int NB, bool BIG>
-__global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
-    constexpr LdsShape SH{W, TB, TA};
-    constexpr int NT = TB * TA * W / 64;
+template <int W, int TB, int TA, int CPT, int WW, int NB, bool BIG>
+__global__ void __launch_bounds__(TB * TA * W / (16 * CPT)) k_lds(LdsArgs a) {
+    constexpr LdsShape SH{W, TB, TA, CPT};
+    constexpr int NT = SH.threads();
     constexpr int CPR = TA * W / 16;
     constexpr int R = SH.reads_per_group();          // reads per group
-    constexpr int GPT = SH.groups() / NT;             // groups per thread
+    constexpr int GPT = SH.groups_per_thread();       // groups per thread
     constexpr int NP = 16 / WW;                       // pieces per chunk
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -249,14 +249,14 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
         const int64_t srow = a.s_b * W;
 
         // Phase 1: HBM -> registers -> LDS.
-        u32x4 v[4];
+        u32x4 v[CPT];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < CPT; ++k) {
             const int cid = t + k * NT;
             v[k] = ld16(st + (cid / CPR) * srow + (cid % CPR) * 16);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < CPT; ++k) {
             const int cid = t + k * NT;
             uint8_t* row = lds + (cid / CPR) * pitch + (cid % CPR) * 16;
             if constexpr (NP == 1) {
@@ -282,6 +282,7 @@ __global__ void __launch_bounds__(TB * TA * W / 64) k_lds(LdsArgs a) {
         // Phase 2: LDS -> registers -> HBM.
 #pragma unroll
         for (int k2 = 0; k2 < GPT; ++k2) {
+            if (SH.groups() % NT != 0 && t + k2 * NT >= SH.groups()) break;
             int col, q;
             lds_group(SH, t, k2, &col, &q);
             const uint8_t* base = lds + (q * R) * pitch + col * SH.read_bytes();
@@ -381,25 +382,26 @@ static int64_t cap_grid(int64_t grid, int64_t block) {
 template <int NB, bool BIG>
 static hipError_t launch_lds(const Plan& p, const LdsArgs& a, hipStream_t st) {
     dim3 grid((unsigned)cap_grid(p.grid, p.block)), block((unsigned)p.block);
-    const int w = p.w, tb = p.tile_b, ta = p.tile_a, ww = p.ww;
-#define TPL_LDS_CASE(W_, TB_, TA_, WW_)                                                             \
-    if (w == W_ && tb == TB_ && ta == TA_ && ww == WW_) {                                            \
-        hipLaunchKernelGGL((k_lds<W_, TB_, TA_, WW_, NB, BIG>), grid, block, p.lds_bytes, st, a);   \
-        return hipGetLastError();                                                                    \
+    const int w = p.w, tb = p.tile_b, ta = p.tile_a, cpt = p.cpt, ww = p.ww;
+#define TPL_LDS_CASE(W_, TB_, TA_, CPT_, WW_)                                                          \
+    if (w == W_ && tb == TB_ && ta == TA_ && cpt == CPT_ && ww == WW_) {                                 \
+        hipLaunchKernelGGL((k_lds<W_, TB_, TA_, CPT_, WW_, NB, BIG>), grid, block, p.lds_bytes, st, a); \
+        return hipGetLastError();                                                                        \
     }
-#define TPL_LDS_SHAPE(W_, TB_, TA_) TPL_LDS_CASE(W_, TB_, TA_, 16) TPL_LDS_CASE(W_, TB_, TA_, 8) TPL_LDS_CASE(W_, TB_, TA_, 4)
-    TPL_LDS_SHAPE(1, 128, 128)
-    TPL_LDS_SHAPE(1, 64, 128)
-    TPL_LDS_SHAPE(2, 256, 64)
-    TPL_LDS_SHAPE(2, 128, 64)
-    TPL_LDS_SHAPE(2, 32, 64)
-    TPL_LDS_SHAPE(4, 64, 64)
-    TPL_LDS_SHAPE(4, 32, 32)
-    TPL_LDS_SHAPE(8, 32, 64)
-    TPL_LDS_SHAPE(8, 16, 32)
-    TPL_LDS_SHAPE(16, 128, 8)
-    TPL_LDS_SHAPE(16, 16, 64)
-    TPL_LDS_SHAPE(16, 16, 16)
+#define TPL_LDS_SHAPE(W_, TB_, TA_, CPT_) \
+    TPL_LDS_CASE(W_, TB_, TA_, CPT_, 16) TPL_LDS_CASE(W_, TB_, TA_, CPT_, 8) TPL_LDS_CASE(W_, TB_, TA_, CPT_, 4)
+    TPL_LDS_SHAPE(1, 128, 128, 2)
+    TPL_LDS_SHAPE(1, 64, 128, 2)
+    TPL_LDS_SHAPE(2, 256, 64, 2)
+    TPL_LDS_SHAPE(2, 128, 64, 2)
+    TPL_LDS_SHAPE(2, 32, 64, 2)
+    TPL_LDS_SHAPE(4, 64, 64, 2)
+    TPL_LDS_SHAPE(4, 32, 32, 2)
+    TPL_LDS_SHAPE(8, 32, 64, 2)
+    TPL_LDS_SHAPE(8, 16, 32, 2)
+    TPL_LDS_SHAPE(16, 128, 8, 2)
+    TPL_LDS_SHAPE(16, 16, 64, 2)
+    TPL_LDS_SHAPE(16, 16, 16, 2)
 #undef TPL_LDS_SHAPE
 #undef TPL_LDS_CASE
     return hipErrorInvalidConfiguration;

@@ -50,7 +50,7 @@ struct Plan {
     int64_t P = 0;
     int k = 0, shift = 0, mask = 0;        // read phase (PAGES32: both phases)
     int k_w = 0, shift_w = 0, mask_w = 0;  // LDS write phase
-    int tile_b = 0, tile_a = 0, pitch = 0, ww = 0;
+    int tile_b = 0, tile_a = 0, cpt = 0, pitch = 0, ww = 0;
     int64_t grid = 0, block = 0;
     int lds_bytes = 0;
     bool big = false;       // 64-bit index math needed

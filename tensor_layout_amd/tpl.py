@@ -59,6 +59,7 @@ class _PlanInfo(ctypes.Structure):
         ("mask_w", ctypes.c_int32),
         ("kernel", ctypes.c_int32),
         ("tile", ctypes.c_int32 * 2),
+        ("chunks_per_thread", ctypes.c_int32),
         ("lds_pitch", ctypes.c_int32),
         ("grid", ctypes.c_int64),
         ("block", ctypes.c_int64),
@@ -81,6 +82,7 @@ class PlanInfo:
     mask_w: int = 0
     kernel: str = "none"
     tile: tuple = (0, 0)
+    chunks_per_thread: int = 0
     lds_pitch: int = 0
     grid: int = 0
     block: int = 0
@@ -160,7 +162,8 @@ def tpl_plan(dtype_bytes: int, extents: Sequence[int], src_strides: Sequence[int
     r = info.rank
     return PlanInfo(st, reason, list(info.extent[:r]), list(info.src_str[:r]), list(info.dst_str[:r]),
                     info.P, info.k, info.shift, info.mask, info.k_w, info.shift_w, info.mask_w,
-                    KERNELS.get(info.kernel, "?"), (info.tile[0], info.tile[1]), info.lds_pitch,
+                    KERNELS.get(info.kernel, "?"), (info.tile[0], info.tile[1]), info.chunks_per_thread,
+                    info.lds_pitch,
                     info.grid, info.block)
 
 

@@ -186,6 +186,8 @@ def conflict_free(addrs, is_write, nbytes):
         used = {}
         for lane in lanes:
             a = addrs[lane]
+            if a is None:
+                continue
             for wd in range(a // 4, a // 4 + max(1, nbytes // 4)):
                 b = wd % banks
                 if b in used and used[b] != wd:
@@ -204,12 +206,16 @@ def test_bank_model_reproduces_measured_tile_maps():
         assert conflict_free(addrs, False, 16) == (pitch in measured_zero), pitch
 
 
-def tile_programs(w, tb, ta, pitch, ww, shift_w, mask_w, shift_r, mask_r):
-    """Yield (is_write, bytes, 64 lane addresses) for every step of both phases."""
-    threads = tb * ta * w // 64
+def tile_programs(w, tb, ta, cpt, pitch, ww, shift_w, mask_w, shift_r, mask_r):
+    """Yield (is_write, bytes, lane addresses) for every step of both phases.
+
+    Lanes without work in a step are left out of the address list's
+    conflict check by giving them None.
+    """
+    threads = tb * ta * w // (16 * cpt)
     cpr = ta * w // 16
     for wave in range(threads // 64):
-        for slot in range(4):
+        for slot in range(cpt):
             for r in range(16 // ww):
                 addrs = []
                 for lane in range(64):
@@ -223,13 +229,17 @@ def tile_programs(w, tb, ta, pitch, ww, shift_w, mask_w, shift_r, mask_r):
     cols = ta if w >= 8 else ta * w // 4
     reads = 16 // w if w >= 8 else 4 * (4 // w if w < 4 else 1)
     rb = w if w >= 8 else 4
-    gpt = cols * nq // threads
+    groups = cols * nq
+    gpt = (groups + threads - 1) // threads
     for wave in range(threads // 64):
         for slot in range(gpt):
             for r in range(reads):
                 addrs = []
                 for lane in range(64):
                     gid = wave * 64 + lane + slot * threads
+                    if gid >= groups:
+                        addrs.append(None)
+                        continue
                     col = (gid // ql) % cols
                     q = (gid // ql // cols) * ql + gid % ql
                     j = r ^ ((lane >> shift_r) & mask_r)
@@ -254,12 +264,13 @@ def test_lds_choice_is_conflict_free(wl):
     assert p.kernel == "lds", p
     tb, ta = p.tile
     ww = 16 if p.lds_pitch % 16 == 0 else 8 if p.lds_pitch % 8 == 0 else 4
-    progs = list(tile_programs(w, tb, ta, p.lds_pitch, ww, p.shift_w, p.mask_w, p.shift, p.mask))
+    cpt = p.chunks_per_thread
+    progs = list(tile_programs(w, tb, ta, cpt, p.lds_pitch, ww, p.shift_w, p.mask_w, p.shift, p.mask))
     assert all(conflict_free(a, wr, nb) for wr, nb, a in progs)
     # no smaller read-phase k would do at this pitch
     for k in range(p.k):
         for shift in range(6 - k, -1, -1):
-            progs = tile_programs(w, tb, ta, p.lds_pitch, ww, p.shift_w, p.mask_w, shift, (1 << k) - 1)
+            progs = tile_programs(w, tb, ta, cpt, p.lds_pitch, ww, p.shift_w, p.mask_w, shift, (1 << k) - 1)
             assert not all(conflict_free(a, wr, nb) for wr, nb, a in progs if not wr)
 
 
@@ -268,5 +279,5 @@ def test_lds_unswizzled_read_would_conflict():
     wl = workloads.TILE_128x64
     p = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, batch=wl.batch)
     assert p.k == 3
-    progs = tile_programs(2, 128, 64, p.lds_pitch, 16, 6, 0, 6, 0)
+    progs = tile_programs(2, 128, 64, p.chunks_per_thread, p.lds_pitch, 16, 6, 0, 6, 0)
     assert not all(conflict_free(a, wr, nb) for wr, nb, a in progs if not wr)
