@@ -106,11 +106,12 @@ struct GatherArgs {
 struct CopyArgs {
     const uint8_t* src;
     uint8_t* dst;
-    int64_t nchunks;     // 16-byte chunks overall
-    FastDiv div_cpr;     // chunks per run
+    int64_t nchunks;     // vectors overall
+    FastDiv div_cpr;     // vectors per run
     int64_t cpr;
     Modes rows;          // the modes outside the contiguous run
     int w;
+    int vec;             // vector bytes: 16, 8 or 4
 };
 
 struct QuadArgs {

@@ -70,17 +70,26 @@ __global__ void __launch_bounds__(256) k_gather(GatherArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Copy: both sides contiguous along one mode; 16-byte chunks of the runs.
+// Copy: both sides contiguous along one mode (the contiguous-chunk case of
+// the dsmem page, "Algorithm" step 1): every run is moved in V-byte vectors,
+// one per lane, one wave per workgroup.
 
-template <int NB, bool BIG>
-__global__ void __launch_bounds__(256) k_copy(CopyArgs a) {
+template <int V> struct Vec;
+template <> struct Vec<4> { typedef uint32_t type; };
+template <> struct Vec<8> { typedef u32x2 type; };
+template <> struct Vec<16> { typedef u32x4 type; };
+
+template <int V, int NB, bool BIG>
+__global__ void __launch_bounds__(64) k_copy(CopyArgs a) {
+    typedef typename Vec<V>::type T;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < a.nchunks; id += stride) {
         int64_t row, c;
         split<BIG>(id, a.cpr, a.div_cpr, row, c);
         int64_t so, d_o;
         modes_offsets<NB, BIG>(a.rows, row, so, d_o);
-        st16(a.dst + d_o * a.w + c * 16, ld16(a.src + so * a.w + c * 16));
+        const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(a.src + so * a.w + c * V));
+        __builtin_nontemporal_store(v, reinterpret_cast<T*>(a.dst + d_o * a.w + c * V));
     }
 }
 
@@ -414,7 +423,10 @@ static hipError_t launch_nb(const Plan& p, const uint8_t* src, uint8_t* dst, hip
         CopyArgs a = p.copy;
         a.src = src;
         a.dst = dst;
-        hipLaunchKernelGGL((k_copy<NB, BIG>), dim3((unsigned)cap_grid(p.grid, 256)), dim3(256), 0, st, a);
+        dim3 grid((unsigned)cap_grid(p.grid, 64)), block(64);
+        if (a.vec == 16) hipLaunchKernelGGL((k_copy<16, NB, BIG>), grid, block, 0, st, a);
+        else if (a.vec == 8) hipLaunchKernelGGL((k_copy<8, NB, BIG>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_copy<4, NB, BIG>), grid, block, 0, st, a);
         return hipGetLastError();
     }
     case TPL_KERNEL_QUAD: {

@@ -504,22 +504,31 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
         return p;
     }
 
-    // Both sides contiguous along the same mode: copy runs.
+    // Both sides contiguous along the same mode: copy runs in the widest
+    // vector (16, 8 or 4 bytes) that divides the run and every run start.
     if (a >= 0 && a == b) {
-        int64_t run = sh.m[a].e * w;
-        if (run % 16 == 0 && sa % 16 == 0 && da % 16 == 0 && all_aligned(sh, a, -1, w, true, 16) &&
-            all_aligned(sh, a, -1, w, false, 16)) {
+        const int64_t run = sh.m[a].e * w;
+        int vec = 0;
+        for (int v : {16, 8, 4}) {
+            if (run % v == 0 && sa % v == 0 && da % v == 0 && all_aligned(sh, a, -1, w, true, v) &&
+                all_aligned(sh, a, -1, w, false, v)) {
+                vec = v;
+                break;
+            }
+        }
+        if (vec) {
             p.kernel = TPL_KERNEL_COPY;
             CopyArgs& c = p.copy;
-            c.cpr = run / 16;
+            c.cpr = run / vec;
             c.div_cpr = make_fastdiv((uint32_t)std::min<int64_t>(c.cpr, 0x7fffffff));
-            c.nchunks = n * w / 16;
+            c.nchunks = n * w / vec;
             c.w = w;
+            c.vec = vec;
             if (c.nchunks >= ((int64_t)1 << 31)) p.big = true;
             set_modes(c.rows, sh, others, no);
-            p.P = 16 / w;
-            p.block = 256;
-            p.grid = std::min<int64_t>((c.nchunks + 255) / 256, 1 << 20);
+            p.P = vec / w > 0 ? vec / w : 1;
+            p.block = 64;
+            p.grid = (c.nchunks + 63) / 64;
             return p;
         }
         choose_gather();

@@ -68,11 +68,16 @@ BF16_16K = Workload("transpose_16384x16384_bf16", 2, (16384, 16384), (16384, 1),
 W16_4K = Workload("transpose_4096x4096_16B", 16, (4096, 4096), (4096, 1), (1, 4096),
                   seed=_seed(5, 1))
 
+# Outer-axis permutation with contiguous inner runs: (64,128,32,32) by axis
+# order (1,0,2,3); both sides keep the last two axes as one 4 KiB run.
+OUTER_PERM = Workload("axes1023_64x128x32x32_f32_runs", 4, (64, 128, 32, 32),
+                      (131072, 1024, 32, 1), (1024, 65536, 32, 1), seed=_seed(6))
+
 # Not a workload of the method: an identity layout (a plain copy) of known
 # size, used to calibrate the HBM byte counters.
 COPY_CALIBRATION = Workload("identity_copy_512MiB_u32", 4, (1 << 27,), (1,), (1,), seed=0x5EED0100)
 
-ALL = [SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)] + [BF16_16K, W16_4K]
+ALL = [SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)] + [BF16_16K, W16_4K, OUTER_PERM]
 
 
 def scaled(wl: Workload, batch: int = None, extents=None) -> Workload:

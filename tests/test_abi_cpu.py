@@ -148,6 +148,7 @@ EXPECTED_KERNEL = {
     "axes0231_64x128x32x32_w8": "lds",
     "transpose_16384x16384_bf16": "lds",
     "transpose_4096x4096_16B": "lds",
+    "axes1023_64x128x32x32_f32_runs": "copy",
 }
 
 

@@ -120,6 +120,8 @@ RAGGED = [
     ("quad_padded", 4, (5, 4, 32), (160, 40, 1), (256, 1, 8), "quad"),
     ("copy_outer_perm", 4, (8, 64, 32), (32, 256, 1), (2048, 32, 1), "copy"),
     ("copy_identity", 2, (1000, 64), (64, 1), (64, 1), "copy"),
+    ("copy_runs_of_8_bytes", 2, (40, 12), (12, 1), (480, 1), "copy"),
+    ("copy_runs_of_4_bytes", 1, (3, 50, 4), (200, 4, 1), (4, 12, 1), "copy"),
     ("gather_unaligned_rows", 2, (130, 1000), (1000, 1), (1, 130), "gather"),
     ("gather_no_unit_stride", 4, (16, 24), (48, 2), (24, 1), "gather"),
     ("gather_small_modes", 8, (3, 5, 7), (35, 7, 1), (1, 3, 15), "gather"),
