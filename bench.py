@@ -95,7 +95,7 @@ def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
     }, y
 
 
-def bench_one(wl, steps, warmup, do_cpu, do_verify):
+def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
     import numpy as np
     import torch
     from tensor_layout_amd import tpl
@@ -112,9 +112,20 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify):
     sp = stream.cuda_stream
     args = (wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch, sp)
     plan = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
+    swz = (plan.k, plan.shift, plan.mask)
+    if entry == "staged":
+        # The staged entry runs the half-wave program on each batch item.
+        hp = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, (0, 0), 1,
+                          geometry=tpl.TPL_GEOM_GFX950_HALFWAVE)
+        swz = (xor_k, 5 - xor_k, (1 << xor_k) - 1) if xor_k >= 0 else (hp.k, hp.shift, hp.mask)
 
     def launch(i):
-        st = tpl.tpl_permute(srcs[i % pairs].data_ptr(), dsts[i % pairs].data_ptr(), *args)
+        if entry == "staged":
+            st = tpl.tpl_permute_staged(srcs[i % pairs].data_ptr(), dsts[i % pairs].data_ptr(), wl.w,
+                                        wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+                                        xor_k, sp)
+        else:
+            st = tpl.tpl_permute(srcs[i % pairs].data_ptr(), dsts[i % pairs].data_ptr(), *args)
         if st != tpl.TPL_OK:
             raise tpl.TplError(st, tpl.tpl_last_error())
 
@@ -156,9 +167,10 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify):
             "elements": wl.elements,
             "element_bytes": wl.w,
             "bytes_per_step": wl.bytes_moved,
-            "kernel": plan.kernel,
-            "tile": list(plan.tile),
-            "k": plan.k, "shift": plan.shift, "mask": plan.mask,
+            "kernel": plan.kernel if entry == "permute" else "staged",
+            "entry": "tpl_permute" if entry == "permute" else f"tpl_permute_staged(xor_k={xor_k})",
+            "tile": list(plan.tile) if entry == "permute" else list(wl.extents),
+            "k": swz[0], "shift": swz[1], "mask": swz[2],
             "buffer_pairs": pairs,
         },
         "roofline": {
@@ -199,6 +211,9 @@ def main():
                     help="with --all: also run the 512 MiB identity copy used to scale HBM counters")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--entry", choices=("permute", "staged"), default="permute",
+                    help="tpl_permute (default) or the half-wave LDS-staged tpl_permute_staged")
+    ap.add_argument("--xor-k", type=int, default=-1, help="staged entry: force this XOR k (-1 = planner's)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); this build has no multi-GPU path.",
@@ -218,7 +233,8 @@ def main():
             print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify)), flush=True)
         return
     wl = by_name[a.workload]
-    print(json.dumps(bench_one(wl, a.steps, a.warmup, not a.no_cpu, not a.no_verify)), flush=True)
+    print(json.dumps(bench_one(wl, a.steps, a.warmup, not a.no_cpu, not a.no_verify, a.entry, a.xor_k)),
+          flush=True)
 
 
 if __name__ == "__main__":

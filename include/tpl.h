@@ -51,7 +51,9 @@ typedef enum {
 enum {
     TPL_GEOM_GFX950 = 0,   /* the kernels this library launches on gfx950 (64-lane waves,
                               LDS banks as measured on MI355X) */
-    TPL_GEOM_PAGES32 = 1   /* the pages' warp program: 32 lanes, 32 banks of 4 bytes */
+    TPL_GEOM_PAGES32 = 1,  /* the pages' warp program: 32 lanes, 32 banks of 4 bytes */
+    TPL_GEOM_GFX950_HALFWAVE = 2  /* the pages' warp program run by one 32-lane half of a
+                                     gfx950 wave on LDS (tpl_permute_staged, tpl_wave.h) */
 };
 
 /* Kernel families a GFX950 plan can pick. */
@@ -119,6 +121,25 @@ int tpl_plan(int dtype_bytes, int rank, const int64_t *extents,
              const int64_t *src_strides, const int64_t *dst_strides,
              const int64_t *elem_offsets, int64_t batch, int geometry,
              tpl_plan_info *out);
+
+/*
+ * The same operation as tpl_permute, executed the way the pages' warp
+ * primitive is (permute_layout page, "Algorithm"): every batch item is moved
+ * by one 32-lane half-wave, which copies the item's source footprint into
+ * LDS, permutes it LDS to LDS with the register-staged, XOR-swizzled
+ * program of tpl_wave.h, and copies the destination footprint back.
+ *
+ * Extra operand rules: prod(extents) = 32 * P with P in {1, 2, 4, 8, 16, 32};
+ * each item's destination footprint is dense (cosize = prod(extents)) and
+ * both footprints fit 8 KiB; otherwise TPL_E_LAYOUT.  xor_k < 0 takes the
+ * smallest conflict-free k of the half-wave bank model (TPL_E_NO_K if none);
+ * xor_k >= 0 forces that k (shift = 5 - k), which lets a caller measure the
+ * unswizzled program.  Source and destination must not overlap.
+ */
+int tpl_permute_staged(const void *src, void *dst, int dtype_bytes, int rank,
+                       const int64_t *extents, const int64_t *src_strides,
+                       const int64_t *dst_strides, const int64_t *elem_offsets,
+                       int64_t batch, int xor_k, hipStream_t stream);
 
 /* Static text of a status code. */
 const char *tpl_status_string(int status);

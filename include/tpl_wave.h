@@ -1,0 +1,81 @@
+/*
+ * tpl_wave.h -- the register-staged, XOR-swizzled permute of one lane group,
+ * as a device function for HIP kernels on gfx950 (header only).
+ *
+ * permute_layout page, "Algorithm" step 3: each lane of a 32-lane group reads
+ * its P elements through the source layout into registers, visiting
+ * iteration j = r ^ ((lane >> shift) & mask) at unrolled step r, where the
+ * iteration n = lane + 32 * j is decomposed row-major over the shard extent
+ * and projected onto the side's strides; after a wave barrier the registers
+ * are written back through the destination layout in the same order.  Both
+ * operands normally live in LDS; src and dst may be the same buffer.
+ *
+ * On a 64-lane gfx950 wave the two half-waves run two independent groups.
+ * For every LDS access width the hardware serves each half-wave in passes of
+ * its own (b32: 32 lanes, b64 reads: 32 lanes, b64 writes: 16 lanes, b128
+ * reads: 16 lanes of one half, b128 writes: 8 lanes), so the bank pattern of
+ * one group is that of the pages' 32-lane warp, and the (shift, mask) that
+ * tpl_plan(..., TPL_GEOM_GFX950_HALFWAVE, ...) returns keeps it free of bank
+ * conflicts.
+ */
+#ifndef TPL_WAVE_H
+#define TPL_WAVE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpl_wave {
+
+/* The shard of one region: row-major iteration extent (last mode fastest)
+ * and per-side strides, in elements; rank <= 8, prod(extent) == 32 * P. */
+struct Shard {
+    int rank;
+    int extent[8];
+    int src_str[8];
+    int dst_str[8];
+};
+
+/* Element offsets of iteration n on both sides. */
+__device__ __forceinline__ void project(const Shard& sh, int n, int* so, int* d_o) {
+    int s = 0, d = 0;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+        if (i >= sh.rank) continue;
+        const int e = sh.extent[i];
+        const int digit = n % e;
+        n /= e;
+        s += digit * sh.src_str[i];
+        d += digit * sh.dst_str[i];
+    }
+    *so = s;
+    *d_o = d;
+}
+
+/* One 32-lane group permutes src into dst (element type T, P elements per
+ * lane).  lane is the lane index inside the group (0..31). */
+template <typename T, int P>
+__device__ __forceinline__ void group_permute(T* dst, const T* src, const Shard& sh, int lane, int shift,
+                                              int mask) {
+    T regs[P];
+    const int key = (lane >> shift) & mask;
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        int so, d_o;
+        project(sh, lane + (r ^ key) * 32, &so, &d_o);
+        regs[r] = src[so];
+    }
+    // Every lane's reads are issued, and their data consumed below, before any
+    // write of this wave reaches LDS: in-place operands are safe.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        int so, d_o;
+        project(sh, lane + (r ^ key) * 32, &so, &d_o);
+        dst[d_o] = regs[r];
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace tpl_wave
+
+#endif /* TPL_WAVE_H */

@@ -485,10 +485,13 @@ static hipError_t launch_big(const Plan& p, const uint8_t* src, uint8_t* dst, hi
 
 static thread_local std::string g_last_error;
 
-static int fail(int status, const std::string& why) {
+// Records the reason text of a non-OK return for tpl_last_error().
+int fail_status(int status, const std::string& why) {
     g_last_error = why;
     return status;
 }
+
+static int fail(int status, const std::string& why) { return fail_status(status, why); }
 
 struct PlanCache {
     std::mutex mu;
@@ -663,6 +666,8 @@ int tpl_plan(int dtype_bytes, int rank, const int64_t* extents, const int64_t* s
             p.reason = "rank must be in 1..8, arrays non-NULL, batch >= 0";
         } else if (geometry == TPL_GEOM_PAGES32) {
             p = tpl::plan_pages32(dtype_bytes, rank, extents, src_strides, dst_strides, batch);
+        } else if (geometry == TPL_GEOM_GFX950_HALFWAVE) {
+            p = tpl::plan_halfwave(dtype_bytes, rank, extents, src_strides, dst_strides, batch);
         } else if (geometry == TPL_GEOM_GFX950) {
             static const int64_t zero[2] = {0, 0};
             p = tpl::plan_gfx950(dtype_bytes, rank, extents, src_strides, dst_strides,

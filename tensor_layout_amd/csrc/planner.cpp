@@ -175,6 +175,18 @@ static void decompose(int64_t n, const Shard& sh, int64_t* digits) {
 
 Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
                   int64_t batch) {
+    return plan_warp32(geometry_pages32(), w, rank, ext, ss, ds, batch);
+}
+
+Plan plan_halfwave(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                   int64_t batch) {
+    return plan_warp32(geometry_gfx950(), w, rank, ext, ss, ds, batch);
+}
+
+// The pages' warp program for one region: 32 lanes, n = lane + 32 j, with
+// the bank model of the given hardware (its first 32 lanes).
+Plan plan_warp32(const Geometry& g, int w, int rank, const int64_t* ext, const int64_t* ss,
+                 const int64_t* ds, int64_t batch) {
     Plan p;
     p.w = w;
     if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) {
@@ -200,8 +212,7 @@ Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const 
         p.reason = "layouts must slice/canonicalize: destination is not one-to-one";
         return p;
     }
-    const Geometry& g = geometry_pages32();
-    const int lanes = g.lanes;
+    const int lanes = 32;
     int64_t total = shard_elements(p.shard);
     if (total % lanes) {
         p.status = TPL_E_LAYOUT;

@@ -75,6 +75,14 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
 Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
                   int64_t batch);
 
+// The same 32-lane program run by one gfx950 half-wave on LDS, with the
+// measured gfx950 bank model.
+Plan plan_halfwave(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                   int64_t batch);
+
+Plan plan_warp32(const Geometry& g, int w, int rank, const int64_t* ext, const int64_t* ss,
+                 const int64_t* ds, int64_t batch);
+
 // Canonical shard (unit modes dropped, neighbours merged where both sides merge).
 Shard make_shard(int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
                  int64_t batch);

@@ -30,11 +30,12 @@ TPL_E_HIP = 8
 
 TPL_GEOM_GFX950 = 0
 TPL_GEOM_PAGES32 = 1
+TPL_GEOM_GFX950_HALFWAVE = 2
 
 KERNELS = {0: "none", 1: "gather", 2: "quad", 3: "lds", 4: "reg16", 5: "copy"}
 MAX_SHARD = 10
 
-EXPORTED = ("tpl_permute", "tpl_plan", "tpl_status_string", "tpl_last_error")
+EXPORTED = ("tpl_permute", "tpl_plan", "tpl_status_string", "tpl_last_error", "tpl_permute_staged")
 
 
 class TplError(RuntimeError):
@@ -116,6 +117,9 @@ def load(path: str = LIB_PATH):
     lib.tpl_permute.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                 i64p, i64p, i64p, i64p, ctypes.c_int64, ctypes.c_void_p]
     lib.tpl_permute.restype = ctypes.c_int
+    lib.tpl_permute_staged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       i64p, i64p, i64p, i64p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.tpl_permute_staged.restype = ctypes.c_int
     lib.tpl_plan.argtypes = [ctypes.c_int, ctypes.c_int, i64p, i64p, i64p, i64p, ctypes.c_int64,
                              ctypes.c_int, ctypes.POINTER(_PlanInfo)]
     lib.tpl_plan.restype = ctypes.c_int
@@ -147,6 +151,17 @@ def tpl_permute(src_ptr: int, dst_ptr: int, dtype_bytes: int, extents: Sequence[
     return lib.tpl_permute(ctypes.c_void_p(src_ptr), ctypes.c_void_p(dst_ptr), int(dtype_bytes),
                            len(extents), _arr(extents), _arr(src_strides), _arr(dst_strides),
                            _arr(elem_offsets), int(batch), ctypes.c_void_p(stream))
+
+
+def tpl_permute_staged(src_ptr: int, dst_ptr: int, dtype_bytes: int, extents: Sequence[int],
+                       src_strides: Sequence[int], dst_strides: Sequence[int],
+                       elem_offsets: Sequence[int] = (0, 0), batch: int = 1, xor_k: int = -1,
+                       stream: int = 0) -> int:
+    """Call the staged (one batch item per half-wave, through LDS) entry point."""
+    lib = load()
+    return lib.tpl_permute_staged(ctypes.c_void_p(src_ptr), ctypes.c_void_p(dst_ptr), int(dtype_bytes),
+                                  len(extents), _arr(extents), _arr(src_strides), _arr(dst_strides),
+                                  _arr(elem_offsets), int(batch), int(xor_k), ctypes.c_void_p(stream))
 
 
 def tpl_plan(dtype_bytes: int, extents: Sequence[int], src_strides: Sequence[int],

@@ -282,3 +282,34 @@ def test_lds_unswizzled_read_would_conflict():
     assert p.k == 3
     progs = tile_programs(2, 128, 64, p.chunks_per_thread, p.lds_pitch, 16, 6, 0, 6, 0)
     assert not all(conflict_free(a, wr, nb) for wr, nb, a in progs if not wr)
+
+
+def test_staged_declines_on_the_host():
+    """tpl_permute_staged checks its operand rules before any device call."""
+    sp, dp = 1 << 20, 1 << 24   # never dereferenced: every call below declines
+    # 8-byte SF tiles: no conflict-free k on the half-wave bank model
+    assert tpl.tpl_permute_staged(sp, dp, 8, (4, 32), (32, 1), (1, 4), (0, 0), 4, -1) == tpl.TPL_E_NO_K
+    # P = 64 is beyond the staged program's register budget
+    assert tpl.tpl_permute_staged(sp, dp, 4, (64, 32), (32, 1), (1, 64), (0, 0), 1, -1) == tpl.TPL_E_LAYOUT
+    # destination footprint with holes
+    assert tpl.tpl_permute_staged(sp, dp, 4, (4, 32), (32, 1), (1, 8), (0, 0), 1, -1) == tpl.TPL_E_LAYOUT
+    # forced k above log2 P
+    assert tpl.tpl_permute_staged(sp, dp, 4, (4, 32), (32, 1), (1, 4), (0, 0), 1, 3) == tpl.TPL_E_ARG
+    # overlapping byte ranges
+    assert tpl.tpl_permute_staged(sp, sp + 64, 4, (4, 32), (32, 1), (1, 4), (0, 0), 4, -1) == tpl.TPL_E_ALIAS
+    assert tpl.tpl_last_error()
+
+
+@pytest.mark.parametrize("w", [1, 2, 4])
+def test_halfwave_plan_of_sf_tiles(w):
+    """The pages' warp program on one gfx950 half-wave: same shard and P as
+    the pages; 4-byte tiles get the pages' shift 3 / mask 3; 1- and 2-byte
+    tiles are admitted too, since lanes sharing a dword do not conflict on
+    gfx950 (they do in the pages' element-granular model)."""
+    p = tpl.tpl_plan(w, (4, 32), (32, 1), (1, 4), geometry=tpl.TPL_GEOM_GFX950_HALFWAVE)
+    q = tpl.tpl_plan(w, (4, 32), (32, 1), (1, 4), geometry=tpl.TPL_GEOM_PAGES32)
+    assert p.ok and p.P == 4 and p.extent == [4, 32]
+    if w == 4:
+        assert (p.k, p.shift, p.mask) == (q.k, q.shift, q.mask) == (2, 3, 3)
+    else:
+        assert q.status == tpl.TPL_E_NO_K
