@@ -107,11 +107,13 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
     srcs = [torch.from_numpy(x).to(dev)]
     for _ in range(pairs - 1):
         srcs.append(srcs[0].clone())
-    dsts = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(pairs)]
+    # In place: each step transposes its buffer again, so a buffer alternates
+    # between the input and its transpose.
+    dsts = srcs if wl.inplace else [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(pairs)]
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    args = (wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch, sp)
-    plan = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
+    plan = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+                        geometry=tpl.TPL_GEOM_GFX950_INPLACE if wl.inplace else tpl.TPL_GEOM_GFX950)
     swz = (plan.k, plan.shift, plan.mask)
     if entry == "staged":
         # The staged entry runs the half-wave program on each batch item.
@@ -119,32 +121,39 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
                           geometry=tpl.TPL_GEOM_GFX950_HALFWAVE)
         swz = (xor_k, 5 - xor_k, (1 << xor_k) - 1) if xor_k >= 0 else (hp.k, hp.shift, hp.mask)
 
+    prepared = tpl.PreparedPermute(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
+    ptrs = [(srcs[i].data_ptr(), dsts[i].data_ptr()) for i in range(pairs)]
+
     def launch(i):
         if entry == "staged":
             st = tpl.tpl_permute_staged(srcs[i % pairs].data_ptr(), dsts[i % pairs].data_ptr(), wl.w,
                                         wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
                                         xor_k, sp)
         else:
-            st = tpl.tpl_permute(srcs[i % pairs].data_ptr(), dsts[i % pairs].data_ptr(), *args)
+            st = prepared(*ptrs[i % pairs], sp)
         if st != tpl.TPL_OK:
             raise tpl.TplError(st, tpl.tpl_last_error())
 
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
-    # One event at every launch boundary, recorded on the launch stream: the
-    # time between two neighbours is one launch (the queue stays full).
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # Two events on the launch stream bracket the K launches; the mean launch
+    # duration is their interval / K (the host enqueues faster than the GPU
+    # drains, so the queue stays full).  An event between every two launches
+    # would add its own packet to each interval (about 1.5 us).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(steps):
-        ev[i].record(stream)
         launch(warmup + i)
-    ev[steps].record(stream)
+    ev1.record(stream)
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kernel_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    avg_ms = sum(kernel_ms) / len(kernel_ms)
+    avg_ms = ev0.elapsed_time(ev1) / steps
+    host_us = (t_enq - t0) * 1e6 / steps
     elapsed = t1 - t0
     value = wl.bytes_moved * steps / elapsed / 1e9
     achieved = wl.bytes_moved / (avg_ms * 1e-3) / 1e9
@@ -181,7 +190,7 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
             "frac": round(achieved / PEAK_GBPS, 4),
             "traffic": traffic_for(wl.name),
             "kernel_ms_avg": round(avg_ms, 5),
-            "kernel_ms_min": round(min(kernel_ms), 5),
+            "host_enqueue_us": round(host_us, 2),
         },
     }
     ref = None
@@ -192,8 +201,16 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
         if ref is None:
             ref = np.empty(nbytes, dtype=np.uint8)
             oracle.permute(x, ref, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
-        last = (warmup + steps - 1) % pairs
-        got = dsts[last].cpu().numpy()
+        if wl.inplace:
+            # one more call on a fresh copy of the input
+            buf = torch.from_numpy(x).to(dev)
+            st = prepared(buf.data_ptr(), buf.data_ptr(), sp)
+            if st != tpl.TPL_OK:
+                raise tpl.TplError(st, tpl.tpl_last_error())
+            got = buf.cpu().numpy()
+        else:
+            last = (warmup + steps - 1) % pairs
+            got = dsts[last].cpu().numpy()
         out["bitexact"] = bool(np.array_equal(got, ref))
     del srcs, dsts
     torch.cuda.empty_cache()
@@ -226,9 +243,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    by_name = {w.name: w for w in workloads.ALL + [workloads.COPY_CALIBRATION]}
+    by_name = {w.name: w for w in workloads.ALL + workloads.INPLACE + [workloads.COPY_CALIBRATION]}
     if a.all:
-        todo = workloads.ALL + ([workloads.COPY_CALIBRATION] if a.with_calibration else [])
+        todo = workloads.ALL + workloads.INPLACE + ([workloads.COPY_CALIBRATION] if a.with_calibration else [])
         for wl in todo:
             print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify)), flush=True)
         return

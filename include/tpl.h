@@ -52,8 +52,11 @@ enum {
     TPL_GEOM_GFX950 = 0,   /* the kernels this library launches on gfx950 (64-lane waves,
                               LDS banks as measured on MI355X) */
     TPL_GEOM_PAGES32 = 1,  /* the pages' warp program: 32 lanes, 32 banks of 4 bytes */
-    TPL_GEOM_GFX950_HALFWAVE = 2  /* the pages' warp program run by one 32-lane half of a
+    TPL_GEOM_GFX950_HALFWAVE = 2, /* the pages' warp program run by one 32-lane half of a
                                      gfx950 wave on LDS (tpl_permute_staged, tpl_wave.h) */
+    TPL_GEOM_GFX950_INPLACE = 3   /* the plan tpl_permute launches when src == dst: a kernel
+                                     whose work units each read before they write, or the
+                                     pair-swap kernel, or TPL_E_ALIAS */
 };
 
 /* Kernel families a GFX950 plan can pick. */
@@ -63,7 +66,8 @@ enum {
     TPL_KERNEL_QUAD = 2,   /* 4x4 fp32 blocks transposed in registers by lane quads (DPP) */
     TPL_KERNEL_LDS = 3,    /* tiled 2-D transpose staged through LDS with XOR-ordered phases */
     TPL_KERNEL_REG16 = 4,  /* 16-byte elements: 8x8 element blocks, pure lane remap */
-    TPL_KERNEL_COPY = 5    /* both sides contiguous along one mode: vector copy of runs */
+    TPL_KERNEL_COPY = 5,   /* both sides contiguous along one mode: vector copy of runs */
+    TPL_KERNEL_SWAP = 6    /* in-place square transpose: mirrored tile pairs swapped through LDS */
 };
 
 #define TPL_MAX_RANK 8
@@ -98,9 +102,14 @@ typedef struct {
  * batch         number of contiguous batch items (>= 0; 0 does nothing).
  * stream        HIP stream (NULL = the null stream).
  *
- * Source and destination may be the same memory only when every work unit's
- * source footprint equals its destination footprint (e.g. an in-place
- * transpose of each batch item); any other overlap returns TPL_E_ALIAS.
+ * Source and destination may be the same memory (equal pointers after the
+ * offsets) when either every work unit's source footprint equals its
+ * destination footprint (e.g. a batch of small in-place transposes), or the
+ * permutation is a square transpose (equal extents and row pitch on the two
+ * transposed modes, batch modes with equal strides on both sides and
+ * disjoint items): then pairs of mirrored tiles are swapped, each pair by one
+ * workgroup that reads both tiles before writing either.  Any other overlap
+ * returns TPL_E_ALIAS.
  * Returns a tpl_status; thread-safe.
  */
 int tpl_permute(const void *src, void *dst, int dtype_bytes, int rank,
@@ -114,7 +123,8 @@ int tpl_permute(const void *src, void *dst, int dtype_bytes, int rank,
  * smallest k whose XOR swizzle makes the read and the write phase
  * bank-conflict-free (declines with TPL_E_NO_K otherwise).  With
  * TPL_GEOM_GFX950 it returns the plan tpl_permute would launch (assuming
- * 256-byte aligned base pointers).  `out` is filled on every return.
+ * 256-byte aligned base pointers), with TPL_GEOM_GFX950_INPLACE the plan it
+ * would launch with src == dst.  `out` is filled on every return.
  * elem_offsets may be NULL.
  */
 int tpl_plan(int dtype_bytes, int rank, const int64_t *extents,

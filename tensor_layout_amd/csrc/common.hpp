@@ -137,6 +137,11 @@ struct LdsArgs {
     Modes batch;
     int32_t pitch;       // LDS row pitch, bytes
     int32_t shift_r, mask_r, shift_w, mask_w;
+    // In-place pair swaps only: tile pairs per batch item, and whether every
+    // tile goes element by element (bases or pitches not 16-byte aligned).
+    int64_t npair;
+    FastDiv div_npair;
+    int32_t scalar;
 };
 
 struct Reg16Args {

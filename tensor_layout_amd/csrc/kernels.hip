@@ -205,14 +205,143 @@ __device__ __forceinline__ void unrotate(uint32_t (&d)[N], int key) {
     }
 }
 
+// Phase 1 of an LDS tile: the TB x TA source tile at st (rows srow bytes
+// apart) through registers into LDS, element (b, a) at b * pitch + a * W.
+// Each thread loads CPT 16-byte chunks, then writes them in 16 / WW pieces
+// whose order is rotated by key_w.
+template <int W, int TB, int TA, int CPT, int WW>
+__device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* st, int64_t srow, int pitch, int t,
+                                            int key_w) {
+    constexpr LdsShape SH{W, TB, TA, CPT};
+    constexpr int NT = SH.threads();
+    constexpr int CPR = TA * W / 16;
+    constexpr int NP = 16 / WW;   // pieces per chunk
+    u32x4 v[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int cid = t + k * NT;
+        v[k] = ld16(st + (cid / CPR) * srow + (cid % CPR) * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int cid = t + k * NT;
+        uint8_t* row = lds + (cid / CPR) * pitch + (cid % CPR) * 16;
+        if constexpr (NP == 1) {
+            *reinterpret_cast<u32x4*>(row) = v[k];
+        } else if constexpr (NP == 2) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int h = r ^ key_w;
+                u32x2 p = h ? u32x2{v[k].z, v[k].w} : u32x2{v[k].x, v[k].y};
+                *reinterpret_cast<u32x2*>(row + h * 8) = p;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = r ^ key_w;
+                uint32_t p = h == 0 ? v[k].x : h == 1 ? v[k].y : h == 2 ? v[k].z : v[k].w;
+                *reinterpret_cast<uint32_t*>(row + h * 4) = p;
+            }
+        }
+    }
+}
+
+// Phase 2 of an LDS tile: LDS through registers to the destination tile at
+// dt (destination rows d_a elements apart).  A thread reads R words of one
+// LDS column, rows in the order r ^ key_r, restores their order, packs them
+// and stores 16-byte destination chunks.
+template <int W, int TB, int TA, int CPT>
+__device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* dt, int64_t d_a, int pitch, int t,
+                                              int key_r) {
+    constexpr LdsShape SH{W, TB, TA, CPT};
+    constexpr int NT = SH.threads();
+    constexpr int R = SH.reads_per_group();       // reads per group
+    constexpr int GPT = SH.groups_per_thread();   // groups per thread
+#pragma unroll
+    for (int k2 = 0; k2 < GPT; ++k2) {
+        if (SH.groups() % NT != 0 && t + k2 * NT >= SH.groups()) break;
+        int col, q;
+        lds_group(SH, t, k2, &col, &q);
+        const uint8_t* base = lds + (q * R) * pitch + col * SH.read_bytes();
+        if constexpr (W == 16) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(base);
+            st16(dt + (int64_t)col * d_a * 16 + q * 16, x);
+        } else if constexpr (W == 8) {
+            uint32_t lo[2], hi[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int j = r ^ key_r;
+                u32x2 x = *reinterpret_cast<const u32x2*>(base + j * pitch);
+                lo[r] = x.x;
+                hi[r] = x.y;
+            }
+            unrotate<2>(lo, key_r);
+            unrotate<2>(hi, key_r);
+            st16(dt + (int64_t)col * d_a * W + q * 16, u32x4{lo[0], hi[0], lo[1], hi[1]});
+        } else {
+            uint32_t d[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int j = r ^ key_r;
+                d[r] = *reinterpret_cast<const uint32_t*>(base + j * pitch);
+            }
+            unrotate<R>(d, key_r);
+            if constexpr (W == 4) {
+                st16(dt + (int64_t)col * d_a * 4 + q * 16, u32x4{d[0], d[1], d[2], d[3]});
+            } else if constexpr (W == 2) {
+                // d[m] = (b0+m, a=2col) | (b0+m, a=2col+1) << 16
+                u32x4 o0, o1;
+                uint32_t* p0 = reinterpret_cast<uint32_t*>(&o0);
+                uint32_t* p1 = reinterpret_cast<uint32_t*>(&o1);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const uint32_t x = d[2 * kk], y = d[2 * kk + 1];
+                    p0[kk] = (x & 0xffffu) | (y << 16);
+                    p1[kk] = (x >> 16) | (y & 0xffff0000u);
+                }
+                uint8_t* out = dt + (int64_t)(2 * col) * d_a * 2 + q * 16;
+                st16(out, o0);
+                st16(out + d_a * 2, o1);
+            } else {
+                // W == 1: d[m] holds bytes (b0+m, a=4col+t), t = 0..3.
+                u32x4 o[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    uint32_t* p = reinterpret_cast<uint32_t*>(&o[tt]);
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int sh = 8 * tt;
+                        p[kk] = ((d[4 * kk] >> sh) & 0xffu) | (((d[4 * kk + 1] >> sh) & 0xffu) << 8) |
+                                (((d[4 * kk + 2] >> sh) & 0xffu) << 16) | (((d[4 * kk + 3] >> sh) & 0xffu) << 24);
+                    }
+                }
+                uint8_t* out = dt + (int64_t)(4 * col) * d_a + q * 16;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) st16(out + tt * d_a, o[tt]);
+            }
+        }
+    }
+}
+
+// One element of W bytes, moved in pieces of min(W, 4) bytes (the LDS pitch
+// and the element bases are multiples of that).
+template <int W>
+__device__ __forceinline__ void copy_elem(uint8_t* d, const uint8_t* s) {
+    if constexpr (W == 1) {
+        *d = *s;
+    } else if constexpr (W == 2) {
+        *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
+    } else {
+#pragma unroll
+        for (int i = 0; i < W / 4; ++i)
+            reinterpret_cast<uint32_t*>(d)[i] = reinterpret_cast<const uint32_t*>(s)[i];
+    }
+}
+
 template <int W, int TB, int TA, int CPT, int WW, int NB, bool BIG>
 __global__ void __launch_bounds__(TB * TA * W / (16 * CPT)) k_lds(LdsArgs a) {
     constexpr LdsShape SH{W, TB, TA, CPT};
     constexpr int NT = SH.threads();
-    constexpr int CPR = TA * W / 16;
-    constexpr int R = SH.reads_per_group();          // reads per group
-    constexpr int GPT = SH.groups_per_thread();       // groups per thread
-    constexpr int NP = 16 / WW;                       // pieces per chunk
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int t = threadIdx.x;
@@ -244,116 +373,94 @@ __global__ void __launch_bounds__(TB * TA * W / (16 * CPT)) k_lds(LdsArgs a) {
                 if (bb >= nb || aa >= na) continue;
                 const uint8_t* s = a.src + (so + (b0 + bb) * a.s_b + a0 + aa) * W;
                 uint8_t* d = a.dst + (d_o + (a0 + aa) * a.d_a + b0 + bb) * W;
-                if constexpr (W == 1) *d = *s;
-                else if constexpr (W == 2) *reinterpret_cast<uint16_t*>(d) = *reinterpret_cast<const uint16_t*>(s);
-                else if constexpr (W == 4) *reinterpret_cast<uint32_t*>(d) = *reinterpret_cast<const uint32_t*>(s);
-                else if constexpr (W == 8) *reinterpret_cast<uint64_t*>(d) = *reinterpret_cast<const uint64_t*>(s);
-                else *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
+                if constexpr (W == 16) *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
+                else copy_elem<W>(d, s);
             }
             continue;   // uniform across the workgroup
         }
 
-        const uint8_t* st = a.src + (so + b0 * a.s_b + a0) * W;
-        uint8_t* dt = a.dst + (d_o + a0 * a.d_a + b0) * W;
-        const int64_t srow = a.s_b * W;
-
-        // Phase 1: HBM -> registers -> LDS.
-        u32x4 v[CPT];
-#pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            const int cid = t + k * NT;
-            v[k] = ld16(st + (cid / CPR) * srow + (cid % CPR) * 16);
-        }
-#pragma unroll
-        for (int k = 0; k < CPT; ++k) {
-            const int cid = t + k * NT;
-            uint8_t* row = lds + (cid / CPR) * pitch + (cid % CPR) * 16;
-            if constexpr (NP == 1) {
-                *reinterpret_cast<u32x4*>(row) = v[k];
-            } else if constexpr (NP == 2) {
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int h = r ^ key_w;
-                    u32x2 p = h ? u32x2{v[k].z, v[k].w} : u32x2{v[k].x, v[k].y};
-                    *reinterpret_cast<u32x2*>(row + h * 8) = p;
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int h = r ^ key_w;
-                    uint32_t p = h == 0 ? v[k].x : h == 1 ? v[k].y : h == 2 ? v[k].z : v[k].w;
-                    *reinterpret_cast<uint32_t*>(row + h * 4) = p;
-                }
-            }
-        }
+        tile_to_lds<W, TB, TA, CPT, WW>(lds, a.src + (so + b0 * a.s_b + a0) * W, a.s_b * W, pitch, t, key_w);
         __syncthreads();
+        tile_from_lds<W, TB, TA, CPT>(lds, a.dst + (d_o + a0 * a.d_a + b0) * W, a.d_a, pitch, t, key_r);
+        __syncthreads();   // LDS is reused by the next tile of this workgroup
+    }
+}
 
-        // Phase 2: LDS -> registers -> HBM.
-#pragma unroll
-        for (int k2 = 0; k2 < GPT; ++k2) {
-            if (SH.groups() % NT != 0 && t + k2 * NT >= SH.groups()) break;
-            int col, q;
-            lds_group(SH, t, k2, &col, &q);
-            const uint8_t* base = lds + (q * R) * pitch + col * SH.read_bytes();
-            if constexpr (W == 16) {
-                const u32x4 x = *reinterpret_cast<const u32x4*>(base);
-                st16(dt + (int64_t)col * a.d_a * 16 + q * 16, x);
-            } else if constexpr (W == 8) {
-                uint32_t lo[2], hi[2];
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int j = r ^ key_r;
-                    u32x2 x = *reinterpret_cast<const u32x2*>(base + j * pitch);
-                    lo[r] = x.x;
-                    hi[r] = x.y;
-                }
-                unrotate<2>(lo, key_r);
-                unrotate<2>(hi, key_r);
-                st16(dt + (int64_t)col * a.d_a * W + q * 16, u32x4{lo[0], hi[0], lo[1], hi[1]});
-            } else {
-                uint32_t d[R];
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int j = r ^ key_r;
-                    d[r] = *reinterpret_cast<const uint32_t*>(base + j * pitch);
-                }
-                unrotate<R>(d, key_r);
-                if constexpr (W == 4) {
-                    st16(dt + (int64_t)col * a.d_a * 4 + q * 16, u32x4{d[0], d[1], d[2], d[3]});
-                } else if constexpr (W == 2) {
-                    // d[m] = (b0+m, a=2col) | (b0+m, a=2col+1) << 16
-                    u32x4 o0, o1;
-                    uint32_t* p0 = reinterpret_cast<uint32_t*>(&o0);
-                    uint32_t* p1 = reinterpret_cast<uint32_t*>(&o1);
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) {
-                        const uint32_t x = d[2 * kk], y = d[2 * kk + 1];
-                        p0[kk] = (x & 0xffffu) | (y << 16);
-                        p1[kk] = (x >> 16) | (y & 0xffff0000u);
-                    }
-                    uint8_t* out = dt + (int64_t)(2 * col) * a.d_a * 2 + q * 16;
-                    st16(out, o0);
-                    st16(out + a.d_a * 2, o1);
-                } else {
-                    // W == 1: d[m] holds bytes (b0+m, a=4col+t), t = 0..3.
-                    u32x4 o[4];
-#pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) {
-                        uint32_t* p = reinterpret_cast<uint32_t*>(&o[tt]);
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk) {
-                            const int sh = 8 * tt;
-                            p[kk] = ((d[4 * kk] >> sh) & 0xffu) | (((d[4 * kk + 1] >> sh) & 0xffu) << 8) |
-                                    (((d[4 * kk + 2] >> sh) & 0xffu) << 16) | (((d[4 * kk + 3] >> sh) & 0xffu) << 24);
-                        }
-                    }
-                    uint8_t* out = dt + (int64_t)(4 * col) * a.d_a + q * 16;
-#pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) st16(out + tt * a.d_a, o[tt]);
-                }
+// In-place square transpose across tiles: tile (b-tile c, a-tile r) and its
+// mirror (b-tile r, a-tile c) occupy each other's destination, so one
+// workgroup reads both into LDS before it writes either.  Work units are the
+// pairs c <= r of every batch item (diagonal tiles pair with themselves);
+// distinct units touch disjoint memory.
+//
+// Unit order: pairs walk the tile diagonals r - c = d, so neighbouring
+// workgroups read different row bands and different column bands (a column
+// band shared by many concurrent workgroups piles their reads onto the same
+// HBM channels when the row pitch is a power of two).  Unit row k of m units
+// holds diagonal k (m - k pairs) followed by diagonal m - k (k pairs); rows
+// k = 0 .. m/2 cover every diagonal once, except that for even m the second
+// half of row m/2 repeats diagonal m/2 and does nothing.
+template <int W, int T, int CPT, int WW, int NB, bool BIG>
+__global__ void __launch_bounds__(T * T * W / (16 * CPT)) k_swap(LdsArgs a) {
+    constexpr LdsShape SH{W, T, T, CPT};
+    constexpr int NT = SH.threads();
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int key_w = (lane >> a.shift_w) & a.mask_w;
+    const int key_r = (lane >> a.shift_r) & a.mask_r;
+    const int pitch = a.pitch;
+    uint8_t* l0 = lds;
+    uint8_t* l1 = lds + T * pitch;
+
+    for (int64_t unit = blockIdx.x; unit < a.ntiles; unit += gridDim.x) {
+        int64_t item, pr, k, j;
+        split<BIG>(unit, a.npair, a.div_npair, item, pr);
+        split<BIG>(pr, a.ntb, a.div_ntb, k, j);
+        const int64_t m = a.ntb;
+        int64_t c, d;
+        if (j < m - k) {
+            d = k;
+            c = j;
+        } else {
+            d = m - k;
+            c = j - (m - k);
+            if (d == k) continue;   // even m, row m/2: diagonal m/2 again (uniform)
+        }
+        const int64_t r = c + d;
+        int64_t so, d_o;
+        modes_offsets<NB, BIG>(a.batch, item, so, d_o);
+        const bool two = c != r;
+        // Tile X: b-tile c, a-tile r.  Tile Y: b-tile r, a-tile c.
+        const int64_t lo = c * T, hi = r * T;
+        const uint8_t* sx = a.src + (so + lo * a.s_b + hi) * W;
+        const uint8_t* sy = a.src + (so + hi * a.s_b + lo) * W;
+        uint8_t* dx = a.dst + (d_o + hi * a.d_a + lo) * W;
+        uint8_t* dy = a.dst + (d_o + lo * a.d_a + hi) * W;
+        if (!a.scalar && hi + T <= a.e_a) {
+            tile_to_lds<W, T, T, CPT, WW>(l0, sx, a.s_b * W, pitch, t, key_w);
+            if (two) tile_to_lds<W, T, T, CPT, WW>(l1, sy, a.s_b * W, pitch, t, key_w);
+            __syncthreads();
+            tile_from_lds<W, T, T, CPT>(l0, dx, a.d_a, pitch, t, key_r);
+            if (two) tile_from_lds<W, T, T, CPT>(l1, dy, a.d_a, pitch, t, key_r);
+        } else {
+            // Ragged (the last tile row and column) or unaligned: element by
+            // element through LDS.  nlo / nhi: valid extents along the modes
+            // whose tile index is c / r.
+            const int nlo = (int)(a.e_a - lo < T ? a.e_a - lo : T), nhi = (int)(a.e_a - hi < T ? a.e_a - hi : T);
+            for (int idx = t; idx < T * T; idx += NT) {
+                const int bb = idx / T, aa = idx % T;
+                if (bb < nlo && aa < nhi) copy_elem<W>(l0 + bb * pitch + aa * W, sx + (bb * a.s_b + aa) * W);
+                if (two && bb < nhi && aa < nlo) copy_elem<W>(l1 + bb * pitch + aa * W, sy + (bb * a.s_b + aa) * W);
+            }
+            __syncthreads();
+            for (int idx = t; idx < T * T; idx += NT) {
+                const int bb = idx % T, aa = idx / T;
+                if (bb < nlo && aa < nhi) copy_elem<W>(dx + (aa * a.d_a + bb) * W, l0 + bb * pitch + aa * W);
+                if (two && bb < nhi && aa < nlo) copy_elem<W>(dy + (aa * a.d_a + bb) * W, l1 + bb * pitch + aa * W);
             }
         }
-        __syncthreads();   // LDS is reused by the next tile of this workgroup
+        __syncthreads();   // LDS is reused by the next pair of this workgroup
     }
 }
 
@@ -417,6 +524,26 @@ static hipError_t launch_lds(const Plan& p, const LdsArgs& a, hipStream_t st) {
 }
 
 template <int NB, bool BIG>
+static hipError_t launch_swap(const Plan& p, const LdsArgs& a, hipStream_t st) {
+    dim3 grid((unsigned)cap_grid(p.grid, p.block)), block((unsigned)p.block);
+    const int w = p.w, tb = p.tile_b, ww = p.ww;
+#define TPL_SWAP_CASE(W_, T_, WW_)                                                                     \
+    if (w == W_ && tb == T_ && ww == WW_) {                                                           \
+        hipLaunchKernelGGL((k_swap<W_, T_, 2, WW_, NB, BIG>), grid, block, p.lds_bytes, st, a);       \
+        return hipGetLastError();                                                                     \
+    }
+#define TPL_SWAP_SHAPE(W_, T_) TPL_SWAP_CASE(W_, T_, 16) TPL_SWAP_CASE(W_, T_, 8) TPL_SWAP_CASE(W_, T_, 4)
+    TPL_SWAP_SHAPE(1, 128)
+    TPL_SWAP_SHAPE(2, 64)
+    TPL_SWAP_SHAPE(4, 64)
+    TPL_SWAP_SHAPE(8, 32)
+    TPL_SWAP_SHAPE(16, 16)
+#undef TPL_SWAP_SHAPE
+#undef TPL_SWAP_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+template <int NB, bool BIG>
 static hipError_t launch_nb(const Plan& p, const uint8_t* src, uint8_t* dst, hipStream_t st) {
     switch (p.kernel) {
     case TPL_KERNEL_COPY: {
@@ -443,6 +570,12 @@ static hipError_t launch_nb(const Plan& p, const uint8_t* src, uint8_t* dst, hip
         a.src = src;
         a.dst = dst;
         return launch_lds<NB, BIG>(p, a, st);
+    }
+    case TPL_KERNEL_SWAP: {
+        LdsArgs a = p.lds;
+        a.src = src;
+        a.dst = dst;
+        return launch_swap<NB, BIG>(p, a, st);
     }
     case TPL_KERNEL_REG16: {
         Reg16Args a = p.reg16;
@@ -519,12 +652,54 @@ static const char* kernel_name(int k) {
     case TPL_KERNEL_LDS: return "lds";
     case TPL_KERNEL_REG16: return "reg16";
     case TPL_KERNEL_COPY: return "copy";
+    case TPL_KERNEL_SWAP: return "swap";
     default: return "none";
     }
 }
 
-static Plan get_plan(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                     const int64_t* offs, int64_t batch, int sa, int da) {
+// The planning inputs of one call, zero-padded to a fixed size so that two
+// calls compare with memcmp.
+struct PlanKey {
+    int32_t w, rank, sa, da, inplace, pad;
+    int64_t ext[TPL_MAX_RANK], ss[TPL_MAX_RANK], ds[TPL_MAX_RANK], offs[2], batch;
+};
+
+static Plan get_plan_shared(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                            const int64_t* offs, int64_t batch, int sa, int da, bool inplace);
+
+// Repeated calls with one layout (the usual case in a loop) skip the shared
+// cache: each thread remembers its last plan of each kind (src != dst, and
+// src == dst).
+static const Plan& get_plan(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                            const int64_t* offs, int64_t batch, int sa, int da, bool inplace = false) {
+    thread_local PlanKey last_key[2];
+    thread_local Plan last_plan[2];
+    thread_local bool have[2] = {false, false};
+    const int slot = inplace ? 1 : 0;
+    PlanKey k;
+    std::memset(&k, 0, sizeof k);
+    k.w = w;
+    k.rank = rank;
+    k.sa = sa;
+    k.da = da;
+    k.inplace = inplace;
+    for (int i = 0; i < rank; ++i) {
+        k.ext[i] = ext[i];
+        k.ss[i] = ss[i];
+        k.ds[i] = ds[i];
+    }
+    k.offs[0] = offs[0];
+    k.offs[1] = offs[1];
+    k.batch = batch;
+    if (have[slot] && std::memcmp(&k, &last_key[slot], sizeof k) == 0) return last_plan[slot];
+    last_plan[slot] = get_plan_shared(w, rank, ext, ss, ds, offs, batch, sa, da, inplace);
+    last_key[slot] = k;
+    have[slot] = true;
+    return last_plan[slot];
+}
+
+static Plan get_plan_shared(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                            const int64_t* offs, int64_t batch, int sa, int da, bool inplace) {
     std::string key;
     key.reserve(64 + rank * 24);
     auto put = [&](int64_t x) { key.append(reinterpret_cast<const char*>(&x), sizeof x); };
@@ -540,13 +715,15 @@ static Plan get_plan(int w, int rank, const int64_t* ext, const int64_t* ss, con
     put(batch);
     put(sa);
     put(da);
+    put(inplace ? 1 : 0);
     PlanCache& c = cache();
     {
         std::lock_guard<std::mutex> lk(c.mu);
         auto it = c.map.find(key);
         if (it != c.map.end()) return it->second;
     }
-    Plan p = plan_gfx950(w, rank, ext, ss, ds, offs, batch, sa, da);
+    Plan p = inplace ? plan_inplace(w, rank, ext, ss, ds, offs, batch, sa, da)
+                     : plan_gfx950(w, rank, ext, ss, ds, offs, batch, sa, da);
     if (log_enabled()) {
         std::fprintf(stderr, "[tpl] plan w=%d kernel=%s status=%d shard=", w, kernel_name(p.kernel), p.status);
         for (int i = 0; i < p.shard.rank; ++i)
@@ -575,33 +752,6 @@ static int64_t cosize_side(const Shard& sh, bool src) {
     return c;
 }
 
-// Overlap is allowed only unit-for-unit: both sides start at one address,
-// every batch item is moved by one work unit that reads all before writing
-// (the planner's unit_is_item), items sit at the same offsets on both sides
-// and do not overlap each other, and an item covers the same span on both
-// sides.
-static bool inplace_ok(const Plan& p, const uint8_t* s, const uint8_t* d) {
-    if (s != d || !p.unit_is_item) return false;
-    const Shard& sh = p.shard;
-    int64_t in_s = 1, in_d = 1;
-    int others = 0;
-    int64_t ostride = 0;
-    for (int i = 0; i < sh.rank; ++i) {
-        if (i == p.mode_a || i == p.mode_b) {
-            in_s += (sh.m[i].e - 1) * sh.m[i].s;
-            in_d += (sh.m[i].e - 1) * sh.m[i].d;
-        } else {
-            if (sh.m[i].s != sh.m[i].d) return false;
-            ++others;
-            ostride = sh.m[i].s;
-        }
-    }
-    if (others > 1) return false;
-    if (in_s != in_d) return false;
-    if (others == 1 && ostride < in_s) return false;
-    return true;
-}
-
 static int permute_impl(const void* src, void* dst, int w, int rank, const int64_t* ext,
                         const int64_t* ss, const int64_t* ds, const int64_t* offs_in, int64_t batch,
                         hipStream_t stream) {
@@ -622,7 +772,7 @@ static int permute_impl(const void* src, void* dst, int w, int rank, const int64
 
     const uint8_t* s = reinterpret_cast<const uint8_t*>(src);
     uint8_t* d = reinterpret_cast<uint8_t*>(dst);
-    Plan p = get_plan(w, rank, ext, ss, ds, offs, batch, ptr_align(src), ptr_align(dst));
+    const Plan& p = get_plan(w, rank, ext, ss, ds, offs, batch, ptr_align(src), ptr_align(dst));
     if (p.status != TPL_OK) return fail(p.status, p.reason);
     if (p.kernel == TPL_KERNEL_NONE) return TPL_OK;
 
@@ -630,10 +780,21 @@ static int permute_impl(const void* src, void* dst, int w, int rank, const int64
     uint8_t* db = d + p.dst_off_bytes;
     const uint8_t* s_hi = sb + cosize_side(p.shard, true) * w;
     const uint8_t* d_hi = db + cosize_side(p.shard, false) * w;
-    if (sb < d_hi && db < s_hi && !inplace_ok(p, sb, db))
-        return fail(TPL_E_ALIAS, "source and destination overlap other than unit-for-unit in place");
+    const Plan* run = &p;
+    if (sb < d_hi && db < s_hi) {
+        if (sb != db) return fail(TPL_E_ALIAS, "source and destination overlap but do not start at one address");
+        if (!inplace_by_unit(p)) {
+            // Same memory on both sides: the in-place plan of the layouts,
+            // planned from the common base (offsets already applied).
+            static const int64_t none[2] = {0, 0};
+            const int al = ptr_align(sb);
+            const Plan& q = get_plan(w, rank, ext, ss, ds, none, batch, al, al, true);
+            if (q.status != TPL_OK) return fail(q.status, q.reason);
+            run = &q;
+        }
+    }
 
-    hipError_t e = p.big ? launch_big<true>(p, sb, db, stream) : launch_big<false>(p, sb, db, stream);
+    hipError_t e = run->big ? launch_big<true>(*run, sb, db, stream) : launch_big<false>(*run, sb, db, stream);
     if (e != hipSuccess) return fail(TPL_E_HIP, std::string("HIP launch failed: ") + hipGetErrorString(e));
     return TPL_OK;
 }
@@ -668,6 +829,10 @@ int tpl_plan(int dtype_bytes, int rank, const int64_t* extents, const int64_t* s
             p = tpl::plan_pages32(dtype_bytes, rank, extents, src_strides, dst_strides, batch);
         } else if (geometry == TPL_GEOM_GFX950_HALFWAVE) {
             p = tpl::plan_halfwave(dtype_bytes, rank, extents, src_strides, dst_strides, batch);
+        } else if (geometry == TPL_GEOM_GFX950_INPLACE) {
+            static const int64_t zero[2] = {0, 0};
+            p = tpl::plan_inplace(dtype_bytes, rank, extents, src_strides, dst_strides,
+                                  elem_offsets ? elem_offsets : zero, batch, 256, 256);
         } else if (geometry == TPL_GEOM_GFX950) {
             static const int64_t zero[2] = {0, 0};
             p = tpl::plan_gfx950(dtype_bytes, rank, extents, src_strides, dst_strides,

@@ -641,6 +641,136 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
     return p;
 }
 
+// Overlap is allowed unit-for-unit: every batch item is moved by one work
+// unit that reads all before writing (the planner's unit_is_item), items sit
+// at the same offsets on both sides and do not overlap each other, and an
+// item covers the same span on both sides.
+bool inplace_by_unit(const Plan& p) {
+    if (!p.unit_is_item || p.src_off_bytes != p.dst_off_bytes) return false;
+    const Shard& sh = p.shard;
+    int64_t in_s = 1, in_d = 1;
+    int others = 0;
+    int64_t ostride = 0;
+    for (int i = 0; i < sh.rank; ++i) {
+        if (i == p.mode_a || i == p.mode_b) {
+            in_s += (sh.m[i].e - 1) * sh.m[i].s;
+            in_d += (sh.m[i].e - 1) * sh.m[i].d;
+        } else {
+            if (sh.m[i].s != sh.m[i].d) return false;
+            ++others;
+            ostride = sh.m[i].s;
+        }
+    }
+    if (others > 1) return false;
+    if (in_s != in_d) return false;
+    if (others == 1 && ostride < in_s) return false;
+    return true;
+}
+
+// Square tiles for in-place pair swaps, one per element width: 128-byte
+// (w <= 2) or 256-byte (w >= 4) rows.
+static const LdsShape kSwapShapes[] = {
+    {1, 128, 128, 2}, {2, 64, 64, 2}, {4, 64, 64, 2}, {8, 32, 32, 2}, {16, 16, 16, 2},
+};
+
+const LdsShape* swap_shapes(int* n) {
+    *n = (int)(sizeof(kSwapShapes) / sizeof(kSwapShapes[0]));
+    return kSwapShapes;
+}
+
+Plan plan_inplace(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                  const int64_t* offs, int64_t batch, int src_align, int dst_align) {
+    Plan p = plan_gfx950(w, rank, ext, ss, ds, offs, batch, src_align, dst_align);
+    if (p.status != TPL_OK || p.kernel == TPL_KERNEL_NONE || inplace_by_unit(p)) return p;
+    auto decline = [&](const char* why) {
+        p.status = TPL_E_ALIAS;
+        p.reason = std::string("source and destination are the same memory: ") + why;
+        p.kernel = TPL_KERNEL_NONE;
+        return p;
+    };
+    if (p.src_off_bytes != p.dst_off_bytes) return decline("offsets differ");
+    const Shard& sh = p.shard;
+    bool identity = true;
+    for (int i = 0; i < sh.rank; ++i) identity = identity && sh.m[i].s == sh.m[i].d;
+    if (identity) {
+        // Every element already sits where the destination layout puts it.
+        p.kernel = TPL_KERNEL_NONE;
+        p.grid = p.block = 0;
+        return p;
+    }
+    const int a = p.mode_a, b = p.mode_b;
+    if (a < 0 || b < 0 || a == b)
+        return decline("only a square transpose of two modes runs in place across tiles");
+    const Mode ma = sh.m[a], mb = sh.m[b];
+    if (ma.e != mb.e || mb.s != ma.d)
+        return decline("the transpose must be square, with one row pitch on both sides");
+    // Every other mode maps each item onto itself, and items are disjoint:
+    // sorted by stride, each mode's stride covers everything inside it.
+    int others[kMaxShard];
+    int no = 0;
+    for (int i = 0; i < sh.rank; ++i) {
+        if (i == a || i == b) continue;
+        if (sh.m[i].s != sh.m[i].d) return decline("batch modes must have equal strides on both sides");
+        others[no++] = i;
+    }
+    std::sort(others, others + no, [&](int x, int y) { return sh.m[x].s < sh.m[y].s; });
+    int64_t span = 1 + (ma.e - 1) * (mb.s + 1);
+    for (int i = 0; i < no; ++i) {
+        const Mode& m = sh.m[others[i]];
+        if (m.s < span) return decline("batch items overlap");
+        span += (m.e - 1) * m.s;
+    }
+    const int sa = std::min(src_align, pow2_align(p.src_off_bytes));
+    if (sa % std::min(w, 4)) return decline("the base is not aligned to the element (or 4 bytes)");
+    const bool vec = sa % 16 == 0 && all_aligned(sh, a, -1, w, true, 16);
+    const LdsShape* pick = nullptr;
+    for (const LdsShape& x : kSwapShapes)
+        if (x.w == w) pick = &x;
+    LdsChoice c = cached_choice(*pick);
+    if (!c.ok) return decline("no bank-conflict-free LDS plan for the square tile");
+
+    const int T = pick->tb;
+    p.kernel = TPL_KERNEL_SWAP;
+    LdsArgs& l = p.lds;
+    l = LdsArgs{};
+    l.e_b = mb.e;
+    l.e_a = ma.e;
+    l.s_b = mb.s;
+    l.d_a = ma.d;
+    l.ntb = l.nta = (ma.e + T - 1) / T;
+    l.npair = (l.ntb / 2 + 1) * l.ntb;   // units per item (diagonal order, see k_swap)
+    l.div_ntb = make_fastdiv((uint32_t)std::min<int64_t>(l.ntb, 0x7fffffff));
+    int64_t items = 1;
+    for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
+    l.ntiles = items * l.npair;
+    if (l.ntiles >= ((int64_t)1 << 31)) p.big = true;
+    l.div_npair = make_fastdiv((uint32_t)std::min<int64_t>(l.npair, 0x7fffffff));
+    set_modes(l.batch, sh, others, no);
+    l.pitch = c.pitch;
+    l.shift_r = c.shift_r;
+    l.mask_r = (1 << c.k_r) - 1;
+    l.shift_w = c.shift_w;
+    l.mask_w = (1 << c.k_w) - 1;
+    l.scalar = vec ? 0 : 1;
+    p.batch_modes = no;
+    p.tile_b = p.tile_a = T;
+    p.cpt = pick->cpt;
+    p.pitch = c.pitch;
+    p.ww = c.ww;
+    p.k = c.k_r;
+    p.shift = c.shift_r;
+    p.mask = l.mask_r;
+    p.k_w = c.k_w;
+    p.shift_w = c.shift_w;
+    p.mask_w = l.mask_w;
+    p.P = pick->reads_per_group();
+    p.block = pick->threads();
+    p.grid = l.ntiles;
+    p.lds_bytes = 2 * T * c.pitch;
+    p.unit_is_item = false;
+    return p;
+}
+
 void fill_info(const Plan& p, tpl_plan_info* out) {
     std::memset(out, 0, sizeof(*out));
     out->status = p.status;

@@ -71,6 +71,18 @@ struct Plan {
 Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
                  const int64_t* offs, int64_t batch, int src_align, int dst_align);
 
+// The plan for src == dst: the device plan when each of its work units reads
+// its whole footprint before writing it; else the pair-swap plan of a square
+// transpose; else TPL_E_ALIAS.
+Plan plan_inplace(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                  const int64_t* offs, int64_t batch, int src_align, int dst_align);
+
+// Does the device plan move every batch item with one read-before-write unit,
+// so that it may run with src == dst?
+bool inplace_by_unit(const Plan& p);
+
+const LdsShape* swap_shapes(int* n);
+
 // The pages' method on one warp region (32 lanes, 32 banks).
 Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
                   int64_t batch);

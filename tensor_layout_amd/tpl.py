@@ -31,8 +31,9 @@ TPL_E_HIP = 8
 TPL_GEOM_GFX950 = 0
 TPL_GEOM_PAGES32 = 1
 TPL_GEOM_GFX950_HALFWAVE = 2
+TPL_GEOM_GFX950_INPLACE = 3
 
-KERNELS = {0: "none", 1: "gather", 2: "quad", 3: "lds", 4: "reg16", 5: "copy"}
+KERNELS = {0: "none", 1: "gather", 2: "quad", 3: "lds", 4: "reg16", 5: "copy", 6: "swap"}
 MAX_SHARD = 10
 
 EXPORTED = ("tpl_permute", "tpl_plan", "tpl_status_string", "tpl_last_error", "tpl_permute_staged")
@@ -151,6 +152,25 @@ def tpl_permute(src_ptr: int, dst_ptr: int, dtype_bytes: int, extents: Sequence[
     return lib.tpl_permute(ctypes.c_void_p(src_ptr), ctypes.c_void_p(dst_ptr), int(dtype_bytes),
                            len(extents), _arr(extents), _arr(src_strides), _arr(dst_strides),
                            _arr(elem_offsets), int(batch), ctypes.c_void_p(stream))
+
+
+class PreparedPermute:
+    """tpl_permute with the layout arguments marshalled once.
+
+    Calling the object with (src_ptr, dst_ptr, stream) makes the same C call
+    as tpl_permute(src_ptr, dst_ptr, dtype_bytes, extents, ...), without
+    rebuilding the ctypes arrays each time; it returns the status code.
+    """
+
+    def __init__(self, dtype_bytes: int, extents: Sequence[int], src_strides: Sequence[int],
+                 dst_strides: Sequence[int], elem_offsets: Sequence[int] = (0, 0), batch: int = 1):
+        self._fn = load().tpl_permute
+        self._args = (int(dtype_bytes), len(extents), _arr(extents), _arr(src_strides), _arr(dst_strides),
+                      _arr(elem_offsets), int(batch))
+
+    def __call__(self, src_ptr: int, dst_ptr: int, stream: int = 0) -> int:
+        w, rank, e, s, d, o, b = self._args
+        return self._fn(src_ptr, dst_ptr, w, rank, e, s, d, o, b, stream)
 
 
 def tpl_permute_staged(src_ptr: int, dst_ptr: int, dtype_bytes: int, extents: Sequence[int],

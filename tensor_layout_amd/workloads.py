@@ -23,6 +23,7 @@ class Workload:
     batch: int = 1
     seed: int = 0
     specials: bool = False   # force fp32 special encodings into the input
+    inplace: bool = False    # source and destination are one buffer
 
     @property
     def elements(self) -> int:
@@ -73,11 +74,15 @@ W16_4K = Workload("transpose_4096x4096_16B", 16, (4096, 4096), (4096, 1), (1, 40
 OUTER_PERM = Workload("axes1023_64x128x32x32_f32_runs", 4, (64, 128, 32, 32),
                       (131072, 1024, 32, 1), (1024, 65536, 32, 1), seed=_seed(6))
 
+# The 16384^2 bf16 transpose with source and destination in one buffer.
+BF16_16K_INPLACE = Workload("transpose_16384x16384_bf16_inplace", 2, (16384, 16384), (16384, 1), (1, 16384),
+                            seed=_seed(5, 2), inplace=True)
 # Not a workload of the method: an identity layout (a plain copy) of known
 # size, used to calibrate the HBM byte counters.
 COPY_CALIBRATION = Workload("identity_copy_512MiB_u32", 4, (1 << 27,), (1,), (1,), seed=0x5EED0100)
 
 ALL = [SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)] + [BF16_16K, W16_4K, OUTER_PERM]
+INPLACE = [BF16_16K_INPLACE]
 
 
 def scaled(wl: Workload, batch: int = None, extents=None) -> Workload:

@@ -313,3 +313,56 @@ def test_halfwave_plan_of_sf_tiles(w):
         assert (p.k, p.shift, p.mask) == (q.k, q.shift, q.mask) == (2, 3, 3)
     else:
         assert q.status == tpl.TPL_E_NO_K
+
+
+# ---------------------------------------------------------------------------
+# in-place planning (src == dst)
+
+G_IN = tpl.TPL_GEOM_GFX950_INPLACE
+
+
+@pytest.mark.parametrize("w,T", [(1, 128), (2, 64), (4, 64), (8, 32), (16, 16)])
+def test_inplace_square_transpose_plans_pair_swaps(w, T):
+    n = 1000
+    p = tpl.tpl_plan(w, (n, n), (n, 1), (1, n), geometry=G_IN)
+    assert p.ok and p.kernel == "swap" and p.tile == (T, T)
+    m = -(-n // T)
+    assert p.grid == (m // 2 + 1) * m          # tile pairs c <= r in diagonal rows of m units
+    q = tpl.tpl_plan(w, (3, n, n), (n * n + 64, n, 1), (n * n + 64, 1, n), geometry=G_IN)
+    assert q.ok and q.kernel == "swap" and q.grid == 3 * p.grid
+
+
+def test_inplace_keeps_read_before_write_kernels():
+    # SF tiles: each batch item is one quad work unit
+    assert tpl.tpl_plan(4, (4, 32), (32, 1), (1, 4), batch=64, geometry=G_IN).kernel == "quad"
+    # one LDS tile
+    assert tpl.tpl_plan(4, (64, 64), (64, 1), (1, 64), geometry=G_IN).kernel == "lds"
+
+
+def test_inplace_identity_is_a_no_op():
+    p = tpl.tpl_plan(4, (64, 128), (128, 1), (128, 1), geometry=G_IN)
+    assert p.ok and p.kernel == "none"
+
+
+@pytest.mark.parametrize("ext,ss,ds,offs,why", [
+    ((100, 200), (200, 1), (1, 100), (0, 0), "square"),                    # not square
+    ((100, 100), (128, 1), (1, 100), (0, 0), "pitch"),                     # pitches differ
+    ((2, 64, 64), (4096, 64, 1), (8192, 1, 64), (0, 0), "batch modes"),    # batch strides differ
+    ((2, 64, 64), (64, 128, 1), (64, 1, 128), (0, 0), "overlap"),          # items interleave
+    ((64, 128), (128, 1), (1, 64), (0, 0), "square"),
+    ((64, 64), (64, 1), (1, 64), (0, 64), "offsets"),                      # offsets differ
+    ((4, 8, 16), (128, 16, 1), (1, 64, 4), (0, 0), "square"),              # 3-mode permute
+])
+def test_inplace_declines(ext, ss, ds, offs, why):
+    p = tpl.tpl_plan(4, ext, ss, ds, offs, geometry=G_IN)
+    assert p.status == tpl.TPL_E_ALIAS
+    assert why in tpl.tpl_last_error()
+
+
+def test_inplace_unaligned_bases_use_element_path_or_decline():
+    # 4-byte elements at a 4-byte aligned offset: planned (element-wise tiles)
+    p = tpl.tpl_plan(4, (100, 100), (100, 1), (1, 100), (3, 3), geometry=G_IN)
+    assert p.ok and p.kernel == "swap"
+    # 8-byte elements at a 4-byte aligned base are still fine (4-byte pieces)
+    p = tpl.tpl_plan(8, (100, 100), (100, 1), (1, 100), (0, 0), geometry=G_IN)
+    assert p.ok

@@ -203,7 +203,7 @@ def test_overlap_other_than_in_place_is_refused():
         # dst starts 64 elements into src
         tpl.permute(buf, buf, (4, 32), (32, 1), (1, 4), src_offset=0, dst_offset=64, batch=8, dtype_bytes=4)
     assert e.value.status == tpl.TPL_E_ALIAS
-    # a square in-place transpose over several tiles moves data across units: refused too
+    # a non-square in-place transpose over several tiles moves data across units: refused too
     with pytest.raises(tpl.TplError) as e:
         tpl.permute(buf, buf, (64, 32), (32, 1), (1, 64), batch=2, dtype_bytes=8)
     assert e.value.status == tpl.TPL_E_ALIAS
