@@ -10,5 +10,5 @@ library never loads it, and it imports nothing from the product.
 * ``plan_oracle`` -- the host-side steps of the method (shard, P, XOR k).
 """
 
-from .runner import address, build, library_path, permute, permute_py  # noqa: F401
+from .runner import address, build, library_path, permute, permute_py, swizzle  # noqa: F401
 from . import plan_oracle  # noqa: F401

@@ -36,6 +36,26 @@
  *
  * The source is snapshotted first when its byte range overlaps the
  * destination's, which gives the read-all-then-write-all result.
+ *
+ * Swizzled operands (oracle_permute_swizzled).  The pages allocate
+ * MMA-compatible tiles whose layout is a plain layout composed with an XOR
+ * swizzle (buffers page, "Pool sugar", alloc_mma) and exclude such operands
+ * from permute_layout ("What it accepts": no swizzle wrapper); they do not
+ * spell the function out.  Here a swizzle is the usual XOR function of the
+ * layout offset, given by three numbers (bits, base, shift):
+ *
+ *   swz(m) = m XOR (((m >> (base + shift)) mod 2^bits) << base)
+ *
+ * i.e. the `bits`-bit field of m starting at bit base + shift is XORed into
+ * the field starting at bit base; with shift >= bits the two fields are
+ * disjoint, so swz is its own inverse.  bits = 0 is the plain layout.  It
+ * acts on the side's layout offset with the batch as an outermost mode,
+ * before the element offset is added:
+ *
+ *   so = off_src + swz_src(b * span_src + sum_i c_i * src_stride_i)
+ *
+ * (when span is a multiple of 2^(base + shift + bits), this equals
+ * swizzling each batch item's offsets on their own).
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -75,18 +95,37 @@ static int64_t layout_apply(int rank, const int64_t *coord, const int64_t *str)
     return m;
 }
 
+/* A swizzle descriptor {bits, base, shift}; NULL or bits == 0 is none. */
+static int swizzle_ok(const int32_t *z)
+{
+    if (!z || z[0] == 0)
+        return 1;
+    return z[0] > 0 && z[0] <= 16 && z[1] >= 0 && z[2] >= z[0] && z[1] + z[2] + z[0] <= 48;
+}
+
+static int64_t swizzle(const int32_t *z, int64_t m)
+{
+    if (!z || z[0] == 0)
+        return m;
+    const int64_t field = (m >> (z[1] + z[2])) & (((int64_t)1 << z[0]) - 1);
+    return m ^ (field << z[1]);
+}
+
 /*
  * src_len / dst_len are the buffer lengths in bytes; every access is checked
  * against them before anything is written.  Returns ORACLE_OK or an error.
  */
-int oracle_permute(const void *src, int64_t src_len, void *dst, int64_t dst_len,
-                   int w, int rank, const int64_t *extents,
-                   const int64_t *src_strides, const int64_t *dst_strides,
-                   const int64_t *elem_offsets, int64_t batch)
+int oracle_permute_swizzled(const void *src, int64_t src_len, void *dst, int64_t dst_len,
+                            int w, int rank, const int64_t *extents,
+                            const int64_t *src_strides, const int64_t *dst_strides,
+                            const int64_t *elem_offsets, int64_t batch,
+                            const int32_t *src_swz, const int32_t *dst_swz)
 {
     if (!src || !dst || !extents || !src_strides || !dst_strides || !elem_offsets)
         return ORACLE_E_ARG;
     if (!width_ok(w) || rank < 1 || rank > 16 || batch < 0)
+        return ORACLE_E_ARG;
+    if (!swizzle_ok(src_swz) || !swizzle_ok(dst_swz))
         return ORACLE_E_ARG;
     int64_t n = batch;
     for (int i = 0; i < rank; ++i) {
@@ -105,8 +144,8 @@ int oracle_permute(const void *src, int64_t src_len, void *dst, int64_t dst_len,
     for (int64_t b = 0; b < batch; ++b) {
         memset(coord, 0, sizeof coord);
         for (;;) {
-            int64_t so = elem_offsets[0] + b * span_s + layout_apply(rank, coord, src_strides);
-            int64_t d_o = elem_offsets[1] + b * span_d + layout_apply(rank, coord, dst_strides);
+            int64_t so = elem_offsets[0] + swizzle(src_swz, b * span_s + layout_apply(rank, coord, src_strides));
+            int64_t d_o = elem_offsets[1] + swizzle(dst_swz, b * span_d + layout_apply(rank, coord, dst_strides));
             if (so < 0 || (so + 1) * w > src_len || d_o < 0 || (d_o + 1) * w > dst_len)
                 return ORACLE_E_RANGE;
             int i = rank - 1;
@@ -137,8 +176,8 @@ int oracle_permute(const void *src, int64_t src_len, void *dst, int64_t dst_len,
     for (int64_t b = 0; b < batch; ++b) {
         memset(coord, 0, sizeof coord);
         for (;;) {
-            int64_t so = elem_offsets[0] + b * span_s + layout_apply(rank, coord, src_strides);
-            int64_t d_o = elem_offsets[1] + b * span_d + layout_apply(rank, coord, dst_strides);
+            int64_t so = elem_offsets[0] + swizzle(src_swz, b * span_s + layout_apply(rank, coord, src_strides));
+            int64_t d_o = elem_offsets[1] + swizzle(dst_swz, b * span_d + layout_apply(rank, coord, dst_strides));
             memcpy(d + d_o * w, s + so * w, (size_t)w);
             int i = rank - 1;
             while (i >= 0 && ++coord[i] == extents[i]) {
@@ -151,6 +190,22 @@ int oracle_permute(const void *src, int64_t src_len, void *dst, int64_t dst_len,
     }
     free(copy);
     return ORACLE_OK;
+}
+
+int oracle_permute(const void *src, int64_t src_len, void *dst, int64_t dst_len,
+                   int w, int rank, const int64_t *extents,
+                   const int64_t *src_strides, const int64_t *dst_strides,
+                   const int64_t *elem_offsets, int64_t batch)
+{
+    return oracle_permute_swizzled(src, src_len, dst, dst_len, w, rank, extents, src_strides,
+                                   dst_strides, elem_offsets, batch, NULL, NULL);
+}
+
+/* The swizzle of one layout offset, exported so tests can pin it. */
+int64_t oracle_swizzle(int32_t bits, int32_t base, int32_t shift, int64_t m)
+{
+    const int32_t z[3] = {bits, base, shift};
+    return swizzle(z, m);
 }
 
 /* Element offset of one coordinate, exported so tests can pin the address

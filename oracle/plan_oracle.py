@@ -152,12 +152,24 @@ def project(idx: Sequence[int], strides: Sequence[int]) -> int:
     return sum(i * s for i, s in zip(idx, strides))
 
 
-def lane_offsets(extent, strides, lanes, P, r, shift, mask) -> List[int]:
+def swizzle_offset(z, m: int) -> int:
+    """An operand's XOR swizzle (bits, base, shift) of a layout offset: the
+    bits-wide field at bit base + shift is XORed into the field at bit base.
+    None or bits == 0: the plain layout.  (The pages allocate such tiles for
+    MMA operands but leave the function to the allocator; this is the usual
+    form.)"""
+    if z is None or z[0] == 0:
+        return m
+    bits, base, shift = z
+    return m ^ (((m >> (base + shift)) & ((1 << bits) - 1)) << base)
+
+
+def lane_offsets(extent, strides, lanes, P, r, shift, mask, swz=None) -> List[int]:
     """Element offset each lane touches at unrolled step r (the per-lane program)."""
     out = []
     for lane in range(lanes):
         j = r ^ ((lane >> shift) & mask)
-        out.append(project(decompose(lane + j * lanes, extent), strides))
+        out.append(swizzle_offset(swz, project(decompose(lane + j * lanes, extent), strides)))
     return out
 
 
@@ -180,9 +192,9 @@ def step_conflict_free(offsets: Sequence[int], w: int, geom: Geometry) -> bool:
     return True
 
 
-def phase_conflict_free(extent, strides, w, lanes, P, shift, mask, geom) -> bool:
+def phase_conflict_free(extent, strides, w, lanes, P, shift, mask, geom, swz=None) -> bool:
     return all(
-        step_conflict_free(lane_offsets(extent, strides, lanes, P, r, shift, mask), w, geom)
+        step_conflict_free(lane_offsets(extent, strides, lanes, P, r, shift, mask, swz), w, geom)
         for r in range(P)
     )
 
@@ -195,14 +207,14 @@ def k_candidates(P: int, lanes: int):
             yield k
 
 
-def choose_xor_k(extent, src_str, dst_str, w, P, geom: Geometry = PAGES32):
+def choose_xor_k(extent, src_str, dst_str, w, P, geom: Geometry = PAGES32, src_swz=None, dst_swz=None):
     """Step 2: smallest k whose (shift, mask) makes both phases conflict-free."""
     lanes = geom.lanes
     for k in k_candidates(P, lanes):
         mask = (1 << k) - 1
         shift = _log2(lanes) - k
-        if (phase_conflict_free(extent, src_str, w, lanes, P, shift, mask, geom)
-                and phase_conflict_free(extent, dst_str, w, lanes, P, shift, mask, geom)):
+        if (phase_conflict_free(extent, src_str, w, lanes, P, shift, mask, geom, src_swz)
+                and phase_conflict_free(extent, dst_str, w, lanes, P, shift, mask, geom, dst_swz)):
             return k, shift, mask
     return None
 
@@ -218,8 +230,11 @@ def dst_injective(extents, dst) -> bool:
     return True
 
 
-def plan(w: int, extents, src_strides, dst_strides, geom: Geometry = PAGES32) -> Plan:
-    """The whole host-side method for one warp region, in the pages' order."""
+def plan(w: int, extents, src_strides, dst_strides, geom: Geometry = PAGES32, src_swz=None,
+         dst_swz=None) -> Plan:
+    """The whole host-side method for one warp region, in the pages' order.
+    Swizzled operands (outside the pages' method): the bank model sees the
+    swizzled offsets."""
     if w not in (1, 2, 4, 8, 16):
         return Plan(False, REASON_WIDTH)
     if any(e < 1 for e in extents):
@@ -235,7 +250,7 @@ def plan(w: int, extents, src_strides, dst_strides, geom: Geometry = PAGES32) ->
     if total % geom.lanes:
         return Plan(False, REASON_LAYOUT, ext, ss, ds)
     P = total // geom.lanes
-    got = choose_xor_k(ext, ss, ds, w, P, geom)
+    got = choose_xor_k(ext, ss, ds, w, P, geom, src_swz, dst_swz)
     if got is None:
         return Plan(False, REASON_NO_K, ext, ss, ds, P)
     k, shift, mask = got

@@ -45,6 +45,14 @@ def _load():
             ctypes.c_int, ctypes.c_int, i64p, i64p, i64p, i64p, ctypes.c_int64,
         ]
         lib.oracle_permute.restype = ctypes.c_int
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_permute_swizzled.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_int, ctypes.c_int, i64p, i64p, i64p, i64p, ctypes.c_int64, i32p, i32p,
+        ]
+        lib.oracle_permute_swizzled.restype = ctypes.c_int
+        lib.oracle_swizzle.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
+        lib.oracle_swizzle.restype = ctypes.c_int64
         lib.oracle_address.argtypes = [ctypes.c_int, i64p, i64p, ctypes.c_int64]
         lib.oracle_address.restype = ctypes.c_int64
         _lib = lib
@@ -56,21 +64,40 @@ def _i64(xs: Sequence[int]):
     return arr
 
 
+def _swz(z):
+    if z is None:
+        return None
+    return (ctypes.c_int32 * 3)(*[int(v) for v in z])
+
+
 def permute(src: np.ndarray, dst: np.ndarray, w: int, extents, src_strides, dst_strides,
-            offsets=(0, 0), batch: int = 1) -> None:
+            offsets=(0, 0), batch: int = 1, src_swizzle=None, dst_swizzle=None) -> None:
     """Run the C oracle on two contiguous byte buffers (``dst`` is written in place).
 
     ``src`` and ``dst`` may be the same array (the oracle snapshots the source).
+    A swizzle is (bits, base, shift) or None.
     """
     lib = _load()
     assert src.flags["C_CONTIGUOUS"] and dst.flags["C_CONTIGUOUS"]
     rank = len(extents)
-    rc = lib.oracle_permute(
-        src.ctypes.data, src.nbytes, dst.ctypes.data, dst.nbytes, int(w), rank,
-        _i64(extents), _i64(src_strides), _i64(dst_strides), _i64(offsets), int(batch),
-    )
+    if src_swizzle is None and dst_swizzle is None:
+        rc = lib.oracle_permute(
+            src.ctypes.data, src.nbytes, dst.ctypes.data, dst.nbytes, int(w), rank,
+            _i64(extents), _i64(src_strides), _i64(dst_strides), _i64(offsets), int(batch),
+        )
+    else:
+        rc = lib.oracle_permute_swizzled(
+            src.ctypes.data, src.nbytes, dst.ctypes.data, dst.nbytes, int(w), rank,
+            _i64(extents), _i64(src_strides), _i64(dst_strides), _i64(offsets), int(batch),
+            _swz(src_swizzle), _swz(dst_swizzle),
+        )
     if rc != 0:
         raise ValueError(f"oracle_permute returned {rc}")
+
+
+def swizzle(bits: int, base: int, shift: int, m: int) -> int:
+    """The oracle's swizzle of one layout offset."""
+    return int(_load().oracle_swizzle(int(bits), int(base), int(shift), int(m)))
 
 
 def address(coord, strides, elem_offset: int = 0) -> int:

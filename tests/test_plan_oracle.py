@@ -155,7 +155,7 @@ def test_result_independent_of_k():
 
 
 def _mutants():
-    def only_read_phase(extent, src_str, dst_str, w, P, geom=po.PAGES32):
+    def only_read_phase(extent, src_str, dst_str, w, P, geom=po.PAGES32, src_swz=None, dst_swz=None):
         lanes = geom.lanes
         for k in po.k_candidates(P, lanes):
             mask, shift = (1 << k) - 1, po._log2(lanes) - k
@@ -163,7 +163,7 @@ def _mutants():
                 return k, shift, mask
         return None
 
-    def shift_off_by_one(extent, src_str, dst_str, w, P, geom=po.PAGES32):
+    def shift_off_by_one(extent, src_str, dst_str, w, P, geom=po.PAGES32, src_swz=None, dst_swz=None):
         lanes = geom.lanes
         for k in po.k_candidates(P, lanes):
             mask, shift = (1 << k) - 1, max(0, po._log2(lanes) - k - 1)
@@ -201,3 +201,36 @@ def test_planted_plan_mistake_is_caught(name, monkeypatch):
     attr, fn = _mutants()[name]
     monkeypatch.setattr(po, attr, fn)
     assert not all(pin() for pin in PINS), name
+
+
+# --------------------------------------------------------------------------
+# swizzled operands (the bank model sees swizzled offsets)
+
+
+def test_swizzle_offset_division_form():
+    from tests.test_oracle_swizzle_pins import swz_divmod
+    rng = np.random.default_rng(17)
+    for _ in range(500):
+        bits = int(rng.integers(1, 5))
+        base = int(rng.integers(0, 5))
+        shift = int(rng.integers(bits, 7))
+        m = int(rng.integers(0, 1 << 30))
+        assert po.swizzle_offset((bits, base, shift), m) == swz_divmod(bits, base, shift, m)
+    assert po.swizzle_offset(None, 77) == 77
+
+
+def test_swizzled_destination_makes_the_transpose_conflict_free_unrotated():
+    """32 x 32 fp32 transpose as one region.  Plain, lane l's write at step j
+    goes to offset j + 32 l, bank j for every lane: only a full XOR (k = 5)
+    spreads it.  With the destination swizzled by (5, 0, 5) the offset is
+    (j ^ l) + 32 l, bank j ^ l, distinct across lanes: k = 0 suffices, and the
+    reads (offset 32 j + l, bank l) stay conflict-free."""
+    p = po.plan(4, (32, 32), (32, 1), (1, 32))
+    assert p.ok and (p.k, p.shift, p.mask) == (5, 0, 31)
+    q = po.plan(4, (32, 32), (32, 1), (1, 32), dst_swz=(5, 0, 5))
+    assert q.ok and q.k == 0
+    # Swizzling the source instead: the read bank becomes l ^ j, so every XOR
+    # that spreads the writes (j depends on the lane) folds the reads together,
+    # and k = 0 leaves the writes on one bank: no k.
+    r = po.plan(4, (32, 32), (32, 1), (1, 32), src_swz=(5, 0, 5))
+    assert not r.ok and r.reason == po.REASON_NO_K
