@@ -80,7 +80,8 @@ def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
     y = np.empty(wl.elements * wl.w, dtype=np.uint8)
     runs, t0 = 0, time.perf_counter()
     while True:
-        oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
+        oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+                       wl.src_swizzle, wl.dst_swizzle)
         runs += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or runs >= max_runs:
@@ -113,22 +114,25 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     plan = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
-                        geometry=tpl.TPL_GEOM_GFX950_INPLACE if wl.inplace else tpl.TPL_GEOM_GFX950)
+                        geometry=tpl.TPL_GEOM_GFX950_INPLACE if wl.inplace else tpl.TPL_GEOM_GFX950,
+                        src_swizzle=wl.src_swizzle, dst_swizzle=wl.dst_swizzle)
     swz = (plan.k, plan.shift, plan.mask)
     if entry == "staged":
         # The staged entry runs the half-wave program on each batch item.
         hp = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, (0, 0), 1,
-                          geometry=tpl.TPL_GEOM_GFX950_HALFWAVE)
+                          geometry=tpl.TPL_GEOM_GFX950_HALFWAVE, src_swizzle=wl.src_swizzle,
+                          dst_swizzle=wl.dst_swizzle)
         swz = (xor_k, 5 - xor_k, (1 << xor_k) - 1) if xor_k >= 0 else (hp.k, hp.shift, hp.mask)
 
-    prepared = tpl.PreparedPermute(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
+    prepared = tpl.PreparedPermute(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+                                   wl.src_swizzle, wl.dst_swizzle)
     ptrs = [(srcs[i].data_ptr(), dsts[i].data_ptr()) for i in range(pairs)]
 
     def launch(i):
         if entry == "staged":
             st = tpl.tpl_permute_staged(srcs[i % pairs].data_ptr(), dsts[i % pairs].data_ptr(), wl.w,
                                         wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
-                                        xor_k, sp)
+                                        xor_k, sp, wl.src_swizzle, wl.dst_swizzle)
         else:
             st = prepared(*ptrs[i % pairs], sp)
         if st != tpl.TPL_OK:
@@ -181,6 +185,8 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
             "tile": list(plan.tile) if entry == "permute" else list(wl.extents),
             "k": swz[0], "shift": swz[1], "mask": swz[2],
             "buffer_pairs": pairs,
+            **({"src_swizzle": list(wl.src_swizzle)} if wl.src_swizzle else {}),
+            **({"dst_swizzle": list(wl.dst_swizzle)} if wl.dst_swizzle else {}),
         },
         "roofline": {
             "bound": "hbm",
@@ -200,7 +206,8 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
         import oracle
         if ref is None:
             ref = np.empty(nbytes, dtype=np.uint8)
-            oracle.permute(x, ref, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch)
+            oracle.permute(x, ref, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+                           wl.src_swizzle, wl.dst_swizzle)
         if wl.inplace:
             # one more call on a fresh copy of the input
             buf = torch.from_numpy(x).to(dev)

@@ -70,6 +70,24 @@ enum {
     TPL_KERNEL_SWAP = 6    /* in-place square transpose: mirrored tile pairs swapped through LDS */
 };
 
+/*
+ * XOR swizzle of an operand (buffers page, "Pool sugar": alloc_mma builds
+ * MMA-compatible tiles as a plain layout composed with a swizzle; the pages
+ * leave its form to the allocator).  The usual XOR function of the layout
+ * offset m, in elements:
+ *
+ *   swz(m) = m XOR (((m >> (base + shift)) mod 2^bits) << base)
+ *
+ * It acts on a side's layout offset with the batch as the outermost mode,
+ * before the element offset is added:
+ *   address = off + swz(b * span + sum_i c_i * stride_i).
+ * bits = 0 is the plain layout; otherwise 1 <= bits <= 16, base >= 0,
+ * shift >= bits (so swz is its own inverse), base + shift + bits <= 48.
+ */
+typedef struct {
+    int32_t bits, base, shift;
+} tpl_swizzle;
+
 #define TPL_MAX_RANK 8
 #define TPL_MAX_SHARD 10
 
@@ -118,6 +136,21 @@ int tpl_permute(const void *src, void *dst, int dtype_bytes, int rank,
                 int64_t batch, hipStream_t stream);
 
 /*
+ * tpl_permute with either side (or both) swizzled (NULL = plain).  Every
+ * element still lands bit for bit at swz_dst(...) of its coordinate.  The
+ * vector kernels are used where each 16-byte access stays inside one
+ * swizzle granule (2^base elements of at least 16 bytes); otherwise the
+ * element-wise kernel runs.  In place (src == dst) only when both layouts
+ * and both swizzles are equal (nothing moves); any other overlap returns
+ * TPL_E_ALIAS.  An invalid swizzle returns TPL_E_ARG.
+ */
+int tpl_permute_swizzled(const void *src, void *dst, int dtype_bytes, int rank,
+                         const int64_t *extents, const int64_t *src_strides,
+                         const int64_t *dst_strides, const int64_t *elem_offsets,
+                         int64_t batch, const tpl_swizzle *src_swizzle,
+                         const tpl_swizzle *dst_swizzle, hipStream_t stream);
+
+/*
  * Host-only planning, no device needed.  With TPL_GEOM_PAGES32 it runs the
  * pages' method on one warp region: shard, P = elements / 32, and the
  * smallest k whose XOR swizzle makes the read and the write phase
@@ -132,6 +165,14 @@ int tpl_plan(int dtype_bytes, int rank, const int64_t *extents,
              const int64_t *elem_offsets, int64_t batch, int geometry,
              tpl_plan_info *out);
 
+/* tpl_plan for swizzled operands (NULL = plain); for PAGES32 and
+ * GFX950_HALFWAVE the bank model sees the swizzled addresses. */
+int tpl_plan_swizzled(int dtype_bytes, int rank, const int64_t *extents,
+                      const int64_t *src_strides, const int64_t *dst_strides,
+                      const int64_t *elem_offsets, int64_t batch,
+                      const tpl_swizzle *src_swizzle, const tpl_swizzle *dst_swizzle,
+                      int geometry, tpl_plan_info *out);
+
 /*
  * The same operation as tpl_permute, executed the way the pages' warp
  * primitive is (permute_layout page, "Algorithm"): every batch item is moved
@@ -140,8 +181,12 @@ int tpl_plan(int dtype_bytes, int rank, const int64_t *extents,
  * program of tpl_wave.h, and copies the destination footprint back.
  *
  * Extra operand rules: prod(extents) = 32 * P with P in {1, 2, 4, 8, 16, 32};
- * each item's destination footprint is dense (cosize = prod(extents)) and
- * both footprints fit 8 KiB; otherwise TPL_E_LAYOUT.  xor_k < 0 takes the
+ * each item's destination footprint is dense (its offsets, swizzled, are
+ * exactly 0 .. prod(extents) - 1) and both footprints fit 8 KiB; with
+ * batch > 1 a swizzled side's item span is a multiple of the swizzle period
+ * 2^(base + shift + bits); otherwise TPL_E_LAYOUT.  Swizzles (NULL = plain)
+ * are applied to the LDS addresses of the program's two phases, and the
+ * bank model plans k on the swizzled addresses.  xor_k < 0 takes the
  * smallest conflict-free k of the half-wave bank model (TPL_E_NO_K if none);
  * xor_k >= 0 forces that k (shift = 5 - k), which lets a caller measure the
  * unswizzled program.  Source and destination must not overlap.
@@ -149,7 +194,8 @@ int tpl_plan(int dtype_bytes, int rank, const int64_t *extents,
 int tpl_permute_staged(const void *src, void *dst, int dtype_bytes, int rank,
                        const int64_t *extents, const int64_t *src_strides,
                        const int64_t *dst_strides, const int64_t *elem_offsets,
-                       int64_t batch, int xor_k, hipStream_t stream);
+                       int64_t batch, const tpl_swizzle *src_swizzle,
+                       const tpl_swizzle *dst_swizzle, int xor_k, hipStream_t stream);
 
 /* Static text of a status code. */
 const char *tpl_status_string(int status);

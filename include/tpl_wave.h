@@ -8,7 +8,9 @@
  * iteration n = lane + 32 * j is decomposed row-major over the shard extent
  * and projected onto the side's strides; after a wave barrier the registers
  * are written back through the destination layout in the same order.  Both
- * operands normally live in LDS; src and dst may be the same buffer.
+ * operands normally live in LDS; src and dst may be the same buffer.  Either
+ * side may be XOR-swizzled (an MMA-style LDS tile): its offsets then go
+ * through swz(m) = m ^ ((m >> shift) & ymask) before the access.
  *
  * On a 64-lane gfx950 wave the two half-waves run two independent groups.
  * For every LDS access width the hardware serves each half-wave in passes of
@@ -35,6 +37,15 @@ struct Shard {
     int dst_str[8];
 };
 
+/* A side's swizzle on element offsets: ymask = (2^bits - 1) << base and
+ * shift is the distance of the XORed field; ymask = 0 is a plain side. */
+struct Swizzle {
+    int ymask;
+    int shift;
+};
+
+__device__ __forceinline__ int swizzle(const Swizzle& z, int m) { return m ^ ((m >> z.shift) & z.ymask); }
+
 /* Element offsets of iteration n on both sides. */
 __device__ __forceinline__ void project(const Shard& sh, int n, int* so, int* d_o) {
     int s = 0, d = 0;
@@ -55,14 +66,14 @@ __device__ __forceinline__ void project(const Shard& sh, int n, int* so, int* d_
  * lane).  lane is the lane index inside the group (0..31). */
 template <typename T, int P>
 __device__ __forceinline__ void group_permute(T* dst, const T* src, const Shard& sh, int lane, int shift,
-                                              int mask) {
+                                              int mask, Swizzle zs = Swizzle{0, 0}, Swizzle zd = Swizzle{0, 0}) {
     T regs[P];
     const int key = (lane >> shift) & mask;
 #pragma unroll
     for (int r = 0; r < P; ++r) {
         int so, d_o;
         project(sh, lane + (r ^ key) * 32, &so, &d_o);
-        regs[r] = src[so];
+        regs[r] = src[swizzle(zs, so)];
     }
     // Every lane's reads are issued, and their data consumed below, before any
     // write of this wave reaches LDS: in-place operands are safe.
@@ -71,7 +82,7 @@ __device__ __forceinline__ void group_permute(T* dst, const T* src, const Shard&
     for (int r = 0; r < P; ++r) {
         int so, d_o;
         project(sh, lane + (r ^ key) * 32, &so, &d_o);
-        dst[d_o] = regs[r];
+        dst[swizzle(zd, d_o)] = regs[r];
     }
     __builtin_amdgcn_wave_barrier();
 }

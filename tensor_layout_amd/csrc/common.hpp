@@ -92,6 +92,20 @@ TPL_HD void modes_offsets(const Modes& m, int64_t idx, int64_t& so, int64_t& d_o
 inline int nb_class(int n) { return n <= 2 ? n : -1; }
 
 // ---------------------------------------------------------------------------
+// XOR swizzle of an operand, on byte offsets from the operand's base (the
+// element swizzle (bits, base, shift) of width-w elements is the byte swizzle
+// (bits, base + log2 w, shift)): P -> P ^ ((P >> shift) & ymask), with ymask
+// = (2^bits - 1) << (base + log2 w).  ymask == 0: plain layout.  Offsets
+// below 2^(base + log2 w) apart inside one aligned granule stay adjacent.
+struct Swz {
+    int64_t ymask;
+    int32_t shift;
+    int32_t pad;
+};
+
+TPL_HD int64_t swz_apply(const Swz& z, int64_t p) { return p ^ ((p >> z.shift) & z.ymask); }
+
+// ---------------------------------------------------------------------------
 // Kernel argument blocks (passed by value).
 
 struct GatherArgs {
@@ -101,6 +115,7 @@ struct GatherArgs {
     Modes modes;     // the whole shard
     int unit;        // bytes moved per access (divides the element width)
     int w;
+    Swz zs, zd;          // operand swizzles (byte form)
 };
 
 struct CopyArgs {
@@ -112,6 +127,7 @@ struct CopyArgs {
     Modes rows;          // the modes outside the contiguous run
     int w;
     int vec;             // vector bytes: 16, 8 or 4
+    Swz zs, zd;          // operand swizzles (byte form)
 };
 
 struct QuadArgs {
@@ -124,6 +140,7 @@ struct QuadArgs {
     int64_t d_a;         // destination stride of the contiguous-source mode (elements)
     int32_t wide;        // 1: 4x32 blocks, lane-ordered 128-byte row loads
     Modes batch;
+    Swz zs, zd;          // operand swizzles (byte form)
 };
 
 struct LdsArgs {
@@ -142,6 +159,7 @@ struct LdsArgs {
     int64_t npair;
     FastDiv div_npair;
     int32_t scalar;
+    Swz zs, zd;          // operand swizzles (byte form)
 };
 
 struct Reg16Args {

@@ -33,6 +33,12 @@ __device__ __forceinline__ void st16(uint8_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
+// base + P, or base + swz(P) for a swizzled operand.
+template <bool SWZ>
+__device__ __forceinline__ uint8_t* at(const uint8_t* base, int64_t p, const Swz& z) {
+    return const_cast<uint8_t*>(base) + (SWZ ? swz_apply(z, p) : p);
+}
+
 template <bool BIG>
 __device__ __forceinline__ void split(int64_t idx, int64_t n, const FastDiv& f, int64_t& q, int64_t& r) {
     if (BIG) {
@@ -63,8 +69,8 @@ __global__ void __launch_bounds__(256) k_gather(GatherArgs a) {
     for (int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; n < a.total; n += stride) {
         int64_t so, d_o;
         modes_offsets<-1, BIG>(a.modes, n, so, d_o);
-        const T* s = reinterpret_cast<const T*>(a.src + so * a.w);
-        T* d = reinterpret_cast<T*>(a.dst + d_o * a.w);
+        const T* s = reinterpret_cast<const T*>(at<true>(a.src, so * a.w, a.zs));
+        T* d = reinterpret_cast<T*>(at<true>(a.dst, d_o * a.w, a.zd));
         for (int u = 0; u < nu; ++u) d[u] = s[u];
     }
 }
@@ -79,7 +85,7 @@ template <> struct Vec<4> { typedef uint32_t type; };
 template <> struct Vec<8> { typedef u32x2 type; };
 template <> struct Vec<16> { typedef u32x4 type; };
 
-template <int V, int NB, bool BIG>
+template <int V, int NB, bool BIG, bool SWZ>
 __global__ void __launch_bounds__(64) k_copy(CopyArgs a) {
     typedef typename Vec<V>::type T;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -88,8 +94,8 @@ __global__ void __launch_bounds__(64) k_copy(CopyArgs a) {
         split<BIG>(id, a.cpr, a.div_cpr, row, c);
         int64_t so, d_o;
         modes_offsets<NB, BIG>(a.rows, row, so, d_o);
-        const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(a.src + so * a.w + c * V));
-        __builtin_nontemporal_store(v, reinterpret_cast<T*>(a.dst + d_o * a.w + c * V));
+        const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(at<SWZ>(a.src, so * a.w + c * V, a.zs)));
+        __builtin_nontemporal_store(v, reinterpret_cast<T*>(at<SWZ>(a.dst, d_o * a.w + c * V, a.zd)));
     }
 }
 
@@ -147,7 +153,7 @@ __device__ __forceinline__ u32x4 transpose4(u32x4 v, int row, int lane) {
     return y;
 }
 
-template <bool WIDE, int NB, bool BIG>
+template <bool WIDE, int NB, bool BIG, bool SWZ>
 __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
     const int lane = threadIdx.x & 63;
     // WIDE: half-wave h takes unit 2g+h; row r = (lane>>3)&3, column group q = lane&7.
@@ -167,11 +173,11 @@ __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
             int64_t so, d_o;
             modes_offsets<NB, BIG>(a.batch, item, so, d_o);
             const int64_t a0 = WIDE ? 32 * ua + 4 * cq : 4 * ua;   // first column this lane loads
-            v = ld16(a.src + (so + r * a.s_b + a0) * 4);
+            v = ld16(at<SWZ>(a.src, (so + r * a.s_b + a0) * 4, a.zs));
             dofs = (d_o + (a0 + r) * a.d_a) * 4;                  // after the exchange: column a0 + r
         }
         const u32x4 y = transpose4<WIDE>(v, r, lane);
-        if (act) st16(a.dst + dofs, y);
+        if (act) st16(at<SWZ>(a.dst, dofs, a.zd), y);
     }
 }
 
@@ -209,9 +215,9 @@ __device__ __forceinline__ void unrotate(uint32_t (&d)[N], int key) {
 // apart) through registers into LDS, element (b, a) at b * pitch + a * W.
 // Each thread loads CPT 16-byte chunks, then writes them in 16 / WW pieces
 // whose order is rotated by key_w.
-template <int W, int TB, int TA, int CPT, int WW>
-__device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* st, int64_t srow, int pitch, int t,
-                                            int key_w) {
+template <int W, int TB, int TA, int CPT, int WW, bool SWZ = false>
+__device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* gsrc, int64_t pt, int64_t srow, int pitch,
+                                            int t, int key_w, const Swz& z = Swz{}) {
     constexpr LdsShape SH{W, TB, TA, CPT};
     constexpr int NT = SH.threads();
     constexpr int CPR = TA * W / 16;
@@ -220,7 +226,7 @@ __device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* st, int
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const int cid = t + k * NT;
-        v[k] = ld16(st + (cid / CPR) * srow + (cid % CPR) * 16);
+        v[k] = ld16(at<SWZ>(gsrc, pt + (cid / CPR) * srow + (cid % CPR) * 16, z));
     }
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
@@ -250,9 +256,9 @@ __device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* st, int
 // dt (destination rows d_a elements apart).  A thread reads R words of one
 // LDS column, rows in the order r ^ key_r, restores their order, packs them
 // and stores 16-byte destination chunks.
-template <int W, int TB, int TA, int CPT>
-__device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* dt, int64_t d_a, int pitch, int t,
-                                              int key_r) {
+template <int W, int TB, int TA, int CPT, bool SWZ = false>
+__device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* gdst, int64_t pt, int64_t d_a, int pitch,
+                                              int t, int key_r, const Swz& z = Swz{}) {
     constexpr LdsShape SH{W, TB, TA, CPT};
     constexpr int NT = SH.threads();
     constexpr int R = SH.reads_per_group();       // reads per group
@@ -265,7 +271,7 @@ __device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* dt, i
         const uint8_t* base = lds + (q * R) * pitch + col * SH.read_bytes();
         if constexpr (W == 16) {
             const u32x4 x = *reinterpret_cast<const u32x4*>(base);
-            st16(dt + (int64_t)col * d_a * 16 + q * 16, x);
+            st16(at<SWZ>(gdst, pt + (int64_t)col * d_a * 16 + q * 16, z), x);
         } else if constexpr (W == 8) {
             uint32_t lo[2], hi[2];
 #pragma unroll
@@ -277,7 +283,7 @@ __device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* dt, i
             }
             unrotate<2>(lo, key_r);
             unrotate<2>(hi, key_r);
-            st16(dt + (int64_t)col * d_a * W + q * 16, u32x4{lo[0], hi[0], lo[1], hi[1]});
+            st16(at<SWZ>(gdst, pt + (int64_t)col * d_a * W + q * 16, z), u32x4{lo[0], hi[0], lo[1], hi[1]});
         } else {
             uint32_t d[R];
 #pragma unroll
@@ -287,7 +293,7 @@ __device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* dt, i
             }
             unrotate<R>(d, key_r);
             if constexpr (W == 4) {
-                st16(dt + (int64_t)col * d_a * 4 + q * 16, u32x4{d[0], d[1], d[2], d[3]});
+                st16(at<SWZ>(gdst, pt + (int64_t)col * d_a * 4 + q * 16, z), u32x4{d[0], d[1], d[2], d[3]});
             } else if constexpr (W == 2) {
                 // d[m] = (b0+m, a=2col) | (b0+m, a=2col+1) << 16
                 u32x4 o0, o1;
@@ -299,9 +305,9 @@ __device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* dt, i
                     p0[kk] = (x & 0xffffu) | (y << 16);
                     p1[kk] = (x >> 16) | (y & 0xffff0000u);
                 }
-                uint8_t* out = dt + (int64_t)(2 * col) * d_a * 2 + q * 16;
-                st16(out, o0);
-                st16(out + d_a * 2, o1);
+                const int64_t out = pt + (int64_t)(2 * col) * d_a * 2 + q * 16;
+                st16(at<SWZ>(gdst, out, z), o0);
+                st16(at<SWZ>(gdst, out + d_a * 2, z), o1);
             } else {
                 // W == 1: d[m] holds bytes (b0+m, a=4col+t), t = 0..3.
                 u32x4 o[4];
@@ -315,9 +321,9 @@ __device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* dt, i
                                 (((d[4 * kk + 2] >> sh) & 0xffu) << 16) | (((d[4 * kk + 3] >> sh) & 0xffu) << 24);
                     }
                 }
-                uint8_t* out = dt + (int64_t)(4 * col) * d_a + q * 16;
+                const int64_t out = pt + (int64_t)(4 * col) * d_a + q * 16;
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) st16(out + tt * d_a, o[tt]);
+                for (int tt = 0; tt < 4; ++tt) st16(at<SWZ>(gdst, out + tt * d_a, z), o[tt]);
             }
         }
     }
@@ -338,11 +344,10 @@ __device__ __forceinline__ void copy_elem(uint8_t* d, const uint8_t* s) {
     }
 }
 
-template <int W, int TB, int TA, int CPT, int WW, int NB, bool BIG>
-__global__ void __launch_bounds__(TB * TA * W / (16 * CPT)) k_lds(LdsArgs a) {
+template <int W, int TB, int TA, int CPT, int WW, int NB, bool BIG, bool SWZ>
+__device__ __forceinline__ void lds_loop(const LdsArgs& a, uint8_t* lds) {
     constexpr LdsShape SH{W, TB, TA, CPT};
     constexpr int NT = SH.threads();
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
@@ -371,19 +376,28 @@ __global__ void __launch_bounds__(TB * TA * W / (16 * CPT)) k_lds(LdsArgs a) {
             for (int idx = t; idx < TB * TA; idx += NT) {
                 const int bb = idx / TA, aa = idx % TA;
                 if (bb >= nb || aa >= na) continue;
-                const uint8_t* s = a.src + (so + (b0 + bb) * a.s_b + a0 + aa) * W;
-                uint8_t* d = a.dst + (d_o + (a0 + aa) * a.d_a + b0 + bb) * W;
+                const uint8_t* s = at<SWZ>(a.src, (so + (b0 + bb) * a.s_b + a0 + aa) * W, a.zs);
+                uint8_t* d = at<SWZ>(a.dst, (d_o + (a0 + aa) * a.d_a + b0 + bb) * W, a.zd);
                 if constexpr (W == 16) *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
                 else copy_elem<W>(d, s);
             }
             continue;   // uniform across the workgroup
         }
 
-        tile_to_lds<W, TB, TA, CPT, WW>(lds, a.src + (so + b0 * a.s_b + a0) * W, a.s_b * W, pitch, t, key_w);
+        tile_to_lds<W, TB, TA, CPT, WW, SWZ>(lds, a.src, (so + b0 * a.s_b + a0) * W, a.s_b * W, pitch, t, key_w,
+                                             a.zs);
         __syncthreads();
-        tile_from_lds<W, TB, TA, CPT>(lds, a.dst + (d_o + a0 * a.d_a + b0) * W, a.d_a, pitch, t, key_r);
+        tile_from_lds<W, TB, TA, CPT, SWZ>(lds, a.dst, (d_o + a0 * a.d_a + b0) * W, a.d_a, pitch, t, key_r, a.zd);
         __syncthreads();   // LDS is reused by the next tile of this workgroup
     }
+}
+
+template <int W, int TB, int TA, int CPT, int WW, int NB, bool BIG>
+__global__ void __launch_bounds__(TB * TA * W / (16 * CPT)) k_lds(LdsArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    // Plain operands take the code without swizzle arithmetic (a uniform branch).
+    if ((a.zs.ymask | a.zd.ymask) == 0) lds_loop<W, TB, TA, CPT, WW, NB, BIG, false>(a, lds);
+    else lds_loop<W, TB, TA, CPT, WW, NB, BIG, true>(a, lds);
 }
 
 // In-place square transpose across tiles: tile (b-tile c, a-tile r) and its
@@ -433,16 +447,18 @@ __global__ void __launch_bounds__(T * T * W / (16 * CPT)) k_swap(LdsArgs a) {
         const bool two = c != r;
         // Tile X: b-tile c, a-tile r.  Tile Y: b-tile r, a-tile c.
         const int64_t lo = c * T, hi = r * T;
-        const uint8_t* sx = a.src + (so + lo * a.s_b + hi) * W;
-        const uint8_t* sy = a.src + (so + hi * a.s_b + lo) * W;
-        uint8_t* dx = a.dst + (d_o + hi * a.d_a + lo) * W;
-        uint8_t* dy = a.dst + (d_o + lo * a.d_a + hi) * W;
+        const int64_t px = (so + lo * a.s_b + hi) * W, py = (so + hi * a.s_b + lo) * W;
+        const int64_t qx = (d_o + hi * a.d_a + lo) * W, qy = (d_o + lo * a.d_a + hi) * W;
+        const uint8_t* sx = a.src + px;
+        const uint8_t* sy = a.src + py;
+        uint8_t* dx = a.dst + qx;
+        uint8_t* dy = a.dst + qy;
         if (!a.scalar && hi + T <= a.e_a) {
-            tile_to_lds<W, T, T, CPT, WW>(l0, sx, a.s_b * W, pitch, t, key_w);
-            if (two) tile_to_lds<W, T, T, CPT, WW>(l1, sy, a.s_b * W, pitch, t, key_w);
+            tile_to_lds<W, T, T, CPT, WW>(l0, a.src, px, a.s_b * W, pitch, t, key_w);
+            if (two) tile_to_lds<W, T, T, CPT, WW>(l1, a.src, py, a.s_b * W, pitch, t, key_w);
             __syncthreads();
-            tile_from_lds<W, T, T, CPT>(l0, dx, a.d_a, pitch, t, key_r);
-            if (two) tile_from_lds<W, T, T, CPT>(l1, dy, a.d_a, pitch, t, key_r);
+            tile_from_lds<W, T, T, CPT>(l0, a.dst, qx, a.d_a, pitch, t, key_r);
+            if (two) tile_from_lds<W, T, T, CPT>(l1, a.dst, qy, a.d_a, pitch, t, key_r);
         } else {
             // Ragged (the last tile row and column) or unaligned: element by
             // element through LDS.  nlo / nhi: valid extents along the modes
@@ -551,9 +567,15 @@ static hipError_t launch_nb(const Plan& p, const uint8_t* src, uint8_t* dst, hip
         a.src = src;
         a.dst = dst;
         dim3 grid((unsigned)cap_grid(p.grid, 64)), block(64);
-        if (a.vec == 16) hipLaunchKernelGGL((k_copy<16, NB, BIG>), grid, block, 0, st, a);
-        else if (a.vec == 8) hipLaunchKernelGGL((k_copy<8, NB, BIG>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_copy<4, NB, BIG>), grid, block, 0, st, a);
+        if ((a.zs.ymask | a.zd.ymask) == 0) {
+            if (a.vec == 16) hipLaunchKernelGGL((k_copy<16, NB, BIG, false>), grid, block, 0, st, a);
+            else if (a.vec == 8) hipLaunchKernelGGL((k_copy<8, NB, BIG, false>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_copy<4, NB, BIG, false>), grid, block, 0, st, a);
+        } else {
+            if (a.vec == 16) hipLaunchKernelGGL((k_copy<16, NB, BIG, true>), grid, block, 0, st, a);
+            else if (a.vec == 8) hipLaunchKernelGGL((k_copy<8, NB, BIG, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_copy<4, NB, BIG, true>), grid, block, 0, st, a);
+        }
         return hipGetLastError();
     }
     case TPL_KERNEL_QUAD: {
@@ -561,8 +583,13 @@ static hipError_t launch_nb(const Plan& p, const uint8_t* src, uint8_t* dst, hip
         a.src = src;
         a.dst = dst;
         dim3 grid((unsigned)cap_grid(p.grid, 64)), block(64);
-        if (a.wide) hipLaunchKernelGGL((k_quad<true, NB, BIG>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_quad<false, NB, BIG>), grid, block, 0, st, a);
+        if ((a.zs.ymask | a.zd.ymask) == 0) {
+            if (a.wide) hipLaunchKernelGGL((k_quad<true, NB, BIG, false>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_quad<false, NB, BIG, false>), grid, block, 0, st, a);
+        } else {
+            if (a.wide) hipLaunchKernelGGL((k_quad<true, NB, BIG, true>), grid, block, 0, st, a);
+            else hipLaunchKernelGGL((k_quad<false, NB, BIG, true>), grid, block, 0, st, a);
+        }
         return hipGetLastError();
     }
     case TPL_KERNEL_LDS: {
@@ -661,17 +688,20 @@ static const char* kernel_name(int k) {
 // calls compare with memcmp.
 struct PlanKey {
     int32_t w, rank, sa, da, inplace, pad;
+    int32_t zs[3], zd[3];
     int64_t ext[TPL_MAX_RANK], ss[TPL_MAX_RANK], ds[TPL_MAX_RANK], offs[2], batch;
 };
 
 static Plan get_plan_shared(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                            const int64_t* offs, int64_t batch, int sa, int da, bool inplace);
+                            const int64_t* offs, int64_t batch, int sa, int da, bool inplace, const SwzSpec& zs,
+                            const SwzSpec& zd);
 
 // Repeated calls with one layout (the usual case in a loop) skip the shared
 // cache: each thread remembers its last plan of each kind (src != dst, and
 // src == dst).
 static const Plan& get_plan(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                            const int64_t* offs, int64_t batch, int sa, int da, bool inplace = false) {
+                            const int64_t* offs, int64_t batch, int sa, int da, bool inplace, const SwzSpec& zs,
+                            const SwzSpec& zd) {
     thread_local PlanKey last_key[2];
     thread_local Plan last_plan[2];
     thread_local bool have[2] = {false, false};
@@ -683,6 +713,12 @@ static const Plan& get_plan(int w, int rank, const int64_t* ext, const int64_t* 
     k.sa = sa;
     k.da = da;
     k.inplace = inplace;
+    k.zs[0] = zs.bits;
+    k.zs[1] = zs.base;
+    k.zs[2] = zs.shift;
+    k.zd[0] = zd.bits;
+    k.zd[1] = zd.base;
+    k.zd[2] = zd.shift;
     for (int i = 0; i < rank; ++i) {
         k.ext[i] = ext[i];
         k.ss[i] = ss[i];
@@ -692,14 +728,15 @@ static const Plan& get_plan(int w, int rank, const int64_t* ext, const int64_t* 
     k.offs[1] = offs[1];
     k.batch = batch;
     if (have[slot] && std::memcmp(&k, &last_key[slot], sizeof k) == 0) return last_plan[slot];
-    last_plan[slot] = get_plan_shared(w, rank, ext, ss, ds, offs, batch, sa, da, inplace);
+    last_plan[slot] = get_plan_shared(w, rank, ext, ss, ds, offs, batch, sa, da, inplace, zs, zd);
     last_key[slot] = k;
     have[slot] = true;
     return last_plan[slot];
 }
 
 static Plan get_plan_shared(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                            const int64_t* offs, int64_t batch, int sa, int da, bool inplace) {
+                            const int64_t* offs, int64_t batch, int sa, int da, bool inplace, const SwzSpec& zs,
+                            const SwzSpec& zd) {
     std::string key;
     key.reserve(64 + rank * 24);
     auto put = [&](int64_t x) { key.append(reinterpret_cast<const char*>(&x), sizeof x); };
@@ -716,14 +753,20 @@ static Plan get_plan_shared(int w, int rank, const int64_t* ext, const int64_t* 
     put(sa);
     put(da);
     put(inplace ? 1 : 0);
+    put(zs.bits);
+    put(zs.base);
+    put(zs.shift);
+    put(zd.bits);
+    put(zd.base);
+    put(zd.shift);
     PlanCache& c = cache();
     {
         std::lock_guard<std::mutex> lk(c.mu);
         auto it = c.map.find(key);
         if (it != c.map.end()) return it->second;
     }
-    Plan p = inplace ? plan_inplace(w, rank, ext, ss, ds, offs, batch, sa, da)
-                     : plan_gfx950(w, rank, ext, ss, ds, offs, batch, sa, da);
+    Plan p = inplace ? plan_inplace(w, rank, ext, ss, ds, offs, batch, sa, da, zs, zd)
+                     : plan_gfx950(w, rank, ext, ss, ds, offs, batch, sa, da, zs, zd);
     if (log_enabled()) {
         std::fprintf(stderr, "[tpl] plan w=%d kernel=%s status=%d shard=", w, kernel_name(p.kernel), p.status);
         for (int i = 0; i < p.shard.rank; ++i)
@@ -752,9 +795,27 @@ static int64_t cosize_side(const Shard& sh, bool src) {
     return c;
 }
 
+// Bytes from a side's base to one past its last byte: the largest swizzled
+// offset is at most the largest plain byte offset with the swizzle mask set.
+static int64_t reach_bytes(const Plan& p, bool src) {
+    const int64_t last = (cosize_side(p.shard, src) - 1) * p.w + (p.w - 1);
+    return (last | swz_bytes(src ? p.zs : p.zd, p.w).ymask) + 1;
+}
+
+static SwzSpec spec_of(const tpl_swizzle* z) {
+    SwzSpec s;
+    if (z) {
+        s.bits = z->bits;
+        s.base = z->base;
+        s.shift = z->shift;
+    }
+    return s;
+}
+
 static int permute_impl(const void* src, void* dst, int w, int rank, const int64_t* ext,
                         const int64_t* ss, const int64_t* ds, const int64_t* offs_in, int64_t batch,
-                        hipStream_t stream) {
+                        const tpl_swizzle* zs_in, const tpl_swizzle* zd_in, hipStream_t stream) {
+    const SwzSpec zs = spec_of(zs_in), zd = spec_of(zd_in);
     if (rank < 1 || rank > TPL_MAX_RANK) return fail(TPL_E_ARG, "rank must be in 1..8");
     if (!ext || !ss || !ds) return fail(TPL_E_ARG, "extents/strides arrays must not be NULL");
     if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16)
@@ -772,14 +833,14 @@ static int permute_impl(const void* src, void* dst, int w, int rank, const int64
 
     const uint8_t* s = reinterpret_cast<const uint8_t*>(src);
     uint8_t* d = reinterpret_cast<uint8_t*>(dst);
-    const Plan& p = get_plan(w, rank, ext, ss, ds, offs, batch, ptr_align(src), ptr_align(dst));
+    const Plan& p = get_plan(w, rank, ext, ss, ds, offs, batch, ptr_align(src), ptr_align(dst), false, zs, zd);
     if (p.status != TPL_OK) return fail(p.status, p.reason);
     if (p.kernel == TPL_KERNEL_NONE) return TPL_OK;
 
     const uint8_t* sb = s + p.src_off_bytes;
     uint8_t* db = d + p.dst_off_bytes;
-    const uint8_t* s_hi = sb + cosize_side(p.shard, true) * w;
-    const uint8_t* d_hi = db + cosize_side(p.shard, false) * w;
+    const uint8_t* s_hi = sb + reach_bytes(p, true);
+    const uint8_t* d_hi = db + reach_bytes(p, false);
     const Plan* run = &p;
     if (sb < d_hi && db < s_hi) {
         if (sb != db) return fail(TPL_E_ALIAS, "source and destination overlap but do not start at one address");
@@ -788,7 +849,7 @@ static int permute_impl(const void* src, void* dst, int w, int rank, const int64
             // planned from the common base (offsets already applied).
             static const int64_t none[2] = {0, 0};
             const int al = ptr_align(sb);
-            const Plan& q = get_plan(w, rank, ext, ss, ds, none, batch, al, al, true);
+            const Plan& q = get_plan(w, rank, ext, ss, ds, none, batch, al, al, true, zs, zd);
             if (q.status != TPL_OK) return fail(q.status, q.reason);
             run = &q;
         }
@@ -811,32 +872,46 @@ int tpl_permute(const void* src, void* dst, int dtype_bytes, int rank, const int
                 int64_t batch, hipStream_t stream) {
     try {
         return tpl::permute_impl(src, dst, dtype_bytes, rank, extents, src_strides, dst_strides,
-                                 elem_offsets, batch, stream);
+                                 elem_offsets, batch, nullptr, nullptr, stream);
     } catch (...) {
         return tpl::fail(TPL_E_ARG, "internal error");
     }
 }
 
-int tpl_plan(int dtype_bytes, int rank, const int64_t* extents, const int64_t* src_strides,
-             const int64_t* dst_strides, const int64_t* elem_offsets, int64_t batch, int geometry,
-             tpl_plan_info* out) {
+int tpl_permute_swizzled(const void* src, void* dst, int dtype_bytes, int rank, const int64_t* extents,
+                         const int64_t* src_strides, const int64_t* dst_strides, const int64_t* elem_offsets,
+                         int64_t batch, const tpl_swizzle* src_swizzle, const tpl_swizzle* dst_swizzle,
+                         hipStream_t stream) {
+    try {
+        return tpl::permute_impl(src, dst, dtype_bytes, rank, extents, src_strides, dst_strides,
+                                 elem_offsets, batch, src_swizzle, dst_swizzle, stream);
+    } catch (...) {
+        return tpl::fail(TPL_E_ARG, "internal error");
+    }
+}
+
+int tpl_plan_swizzled(int dtype_bytes, int rank, const int64_t* extents, const int64_t* src_strides,
+                      const int64_t* dst_strides, const int64_t* elem_offsets, int64_t batch,
+                      const tpl_swizzle* src_swizzle, const tpl_swizzle* dst_swizzle, int geometry,
+                      tpl_plan_info* out) {
     try {
         tpl::Plan p;
+        static const int64_t zero[2] = {0, 0};
+        const int64_t* offs = elem_offsets ? elem_offsets : zero;
+        const tpl::SwzSpec zs = tpl::spec_of(src_swizzle), zd = tpl::spec_of(dst_swizzle);
         if (rank < 1 || rank > TPL_MAX_RANK || !extents || !src_strides || !dst_strides || batch < 0) {
             p.status = TPL_E_ARG;
             p.reason = "rank must be in 1..8, arrays non-NULL, batch >= 0";
         } else if (geometry == TPL_GEOM_PAGES32) {
-            p = tpl::plan_pages32(dtype_bytes, rank, extents, src_strides, dst_strides, batch);
+            p = tpl::plan_pages32(dtype_bytes, rank, extents, src_strides, dst_strides, batch, zs, zd);
         } else if (geometry == TPL_GEOM_GFX950_HALFWAVE) {
-            p = tpl::plan_halfwave(dtype_bytes, rank, extents, src_strides, dst_strides, batch);
+            p = tpl::plan_halfwave(dtype_bytes, rank, extents, src_strides, dst_strides, batch, zs, zd);
         } else if (geometry == TPL_GEOM_GFX950_INPLACE) {
-            static const int64_t zero[2] = {0, 0};
-            p = tpl::plan_inplace(dtype_bytes, rank, extents, src_strides, dst_strides,
-                                  elem_offsets ? elem_offsets : zero, batch, 256, 256);
+            p = tpl::plan_inplace(dtype_bytes, rank, extents, src_strides, dst_strides, offs, batch, 256, 256, zs,
+                                  zd);
         } else if (geometry == TPL_GEOM_GFX950) {
-            static const int64_t zero[2] = {0, 0};
-            p = tpl::plan_gfx950(dtype_bytes, rank, extents, src_strides, dst_strides,
-                                 elem_offsets ? elem_offsets : zero, batch, 256, 256);
+            p = tpl::plan_gfx950(dtype_bytes, rank, extents, src_strides, dst_strides, offs, batch, 256, 256, zs,
+                                 zd);
         } else {
             p.status = TPL_E_ARG;
             p.reason = "unknown geometry";
@@ -847,6 +922,13 @@ int tpl_plan(int dtype_bytes, int rank, const int64_t* extents, const int64_t* s
     } catch (...) {
         return tpl::fail(TPL_E_ARG, "internal error");
     }
+}
+
+int tpl_plan(int dtype_bytes, int rank, const int64_t* extents, const int64_t* src_strides,
+             const int64_t* dst_strides, const int64_t* elem_offsets, int64_t batch, int geometry,
+             tpl_plan_info* out) {
+    return tpl_plan_swizzled(dtype_bytes, rank, extents, src_strides, dst_strides, elem_offsets, batch, nullptr,
+                             nullptr, geometry, out);
 }
 
 const char* tpl_status_string(int status) {

@@ -174,24 +174,39 @@ static void decompose(int64_t n, const Shard& sh, int64_t* digits) {
 }
 
 Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                  int64_t batch) {
-    return plan_warp32(geometry_pages32(), w, rank, ext, ss, ds, batch);
+                  int64_t batch, const SwzSpec& zs, const SwzSpec& zd) {
+    return plan_warp32(geometry_pages32(), w, rank, ext, ss, ds, batch, zs, zd);
 }
 
 Plan plan_halfwave(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                   int64_t batch) {
-    return plan_warp32(geometry_gfx950(), w, rank, ext, ss, ds, batch);
+                   int64_t batch, const SwzSpec& zs, const SwzSpec& zd) {
+    return plan_warp32(geometry_gfx950(), w, rank, ext, ss, ds, batch, zs, zd);
+}
+
+// A swizzle applied to an element offset.
+static int64_t swz_elem(const SwzSpec& z, int64_t m) {
+    if (z.bits == 0) return m;
+    return m ^ (((m >> (z.base + z.shift)) & (((int64_t)1 << z.bits) - 1)) << z.base);
 }
 
 // The pages' warp program for one region: 32 lanes, n = lane + 32 j, with
-// the bank model of the given hardware (its first 32 lanes).
+// the bank model of the given hardware (its first 32 lanes).  Swizzled
+// operands: each side's offsets go through its swizzle before the bank model
+// sees them.
 Plan plan_warp32(const Geometry& g, int w, int rank, const int64_t* ext, const int64_t* ss,
-                 const int64_t* ds, int64_t batch) {
+                 const int64_t* ds, int64_t batch, const SwzSpec& zs, const SwzSpec& zd) {
     Plan p;
     p.w = w;
+    p.zs = zs;
+    p.zd = zd;
     if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) {
         p.status = TPL_E_DTYPE_WIDTH;
         p.reason = "unsupported dtype byte width";
+        return p;
+    }
+    if (!swz_valid(zs) || !swz_valid(zd)) {
+        p.status = TPL_E_ARG;
+        p.reason = "a swizzle needs 0 <= bits <= 16, base >= 0, shift >= bits and base + shift + bits <= 48";
         return p;
     }
     for (int i = 0; i < rank; ++i) {
@@ -237,7 +252,7 @@ Plan plan_warp32(const Geometry& g, int w, int rank, const int64_t* ext, const i
                     int64_t off = 0;
                     for (int i = 0; i < p.shard.rank; ++i)
                         off += digits[i] * (phase == 0 ? p.shard.m[i].s : p.shard.m[i].d);
-                    addr[lane] = off * w;
+                    addr[lane] = swz_elem(phase == 0 ? zs : zd, off) * w;
                 }
                 ok = step_conflict_free(g, phase == 1, w, addr, nullptr, lanes);
             }
@@ -395,10 +410,15 @@ bool count_elements(int rank, const int64_t* ext, int64_t batch, int64_t* out) {
     return true;
 }
 
-Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                 const int64_t* offs, int64_t batch, int src_align, int dst_align) {
+// granule_s / granule_d: bytes that stay adjacent under each side's swizzle
+// (a vector access must not straddle one); 1 << 30 for a plain side.
+static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                      const int64_t* offs, int64_t batch, int src_align, int dst_align, int64_t granule_s,
+                      int64_t granule_d) {
     Plan p;
     p.w = w;
+    const bool plain = granule_s >= ((int64_t)1 << 30) && granule_d >= ((int64_t)1 << 30);
+    const bool vec16 = granule_s >= 16 && granule_d >= 16;
     if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) {
         p.status = TPL_E_DTYPE_WIDTH;
         p.reason = "unsupported dtype byte width (must be 1, 2, 4, 8 or 16)";
@@ -489,7 +509,7 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
 
     // 16-byte elements too small for an LDS tile: one element is one dwordx4;
     // lanes form 8x8 blocks.
-    if (w == 16 && a >= 0 && b >= 0 && a != b && sa % 16 == 0 && da % 16 == 0 &&
+    if (plain && w == 16 && a >= 0 && b >= 0 && a != b && sa % 16 == 0 && da % 16 == 0 &&
         (sh.m[b].e < 16 || sh.m[a].e < 16)) {
         p.kernel = TPL_KERNEL_REG16;
         Reg16Args& r = p.reg16;
@@ -521,7 +541,7 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
         const int64_t run = sh.m[a].e * w;
         int vec = 0;
         for (int v : {16, 8, 4}) {
-            if (run % v == 0 && sa % v == 0 && da % v == 0 && all_aligned(sh, a, -1, w, true, v) &&
+            if (v <= granule_s && v <= granule_d && run % v == 0 && sa % v == 0 && da % v == 0 && all_aligned(sh, a, -1, w, true, v) &&
                 all_aligned(sh, a, -1, w, false, v)) {
                 vec = v;
                 break;
@@ -552,7 +572,7 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
         bool src_ok = sa % 16 == 0 && all_aligned(sh, a, -1, w, true, 16);
         bool dst_ok = da % 16 == 0 && all_aligned(sh, b, -1, w, false, 16);
         // 4x4 fp32 blocks transposed inside lane quads.
-        if (w == 4 && mb.e == 4 && ma.e % 4 == 0 && src_ok && dst_ok) {
+        if (vec16 && w == 4 && mb.e == 4 && ma.e % 4 == 0 && src_ok && dst_ok) {
             p.kernel = TPL_KERNEL_QUAD;
             QuadArgs& q = p.quad;
             // Wide units (4 rows x 32 columns, one per 32-lane half-wave) when the
@@ -579,7 +599,7 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
             return p;
         }
         // Tiled LDS transpose.
-        if (ma.e * w >= 64 && mb.e * w >= 64 && src_ok && dst_ok) {
+        if (vec16 && ma.e * w >= 64 && mb.e * w >= 64 && src_ok && dst_ok) {
             const LdsShape* pick = nullptr;
             for (const LdsShape& s : kLdsShapes) {
                 if (s.w != w) continue;
@@ -641,6 +661,59 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
     return p;
 }
 
+static int log2_width(int w) {
+    int l = 0;
+    while ((1 << l) < w) ++l;
+    return l;
+}
+
+Swz swz_bytes(const SwzSpec& z, int w) {
+    Swz b{};
+    if (z.bits > 0) {
+        b.ymask = (((int64_t)1 << z.bits) - 1) << (z.base + log2_width(w));
+        b.shift = z.shift;
+    }
+    return b;
+}
+
+bool swz_valid(const SwzSpec& z) {
+    if (z.bits == 0) return true;
+    return z.bits > 0 && z.bits <= 16 && z.base >= 0 && z.shift >= z.bits && z.base + z.shift + z.bits <= 48;
+}
+
+Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                 const int64_t* offs, int64_t batch, int src_align, int dst_align, const SwzSpec& zs,
+                 const SwzSpec& zd) {
+    if (!swz_valid(zs) || !swz_valid(zd)) {
+        Plan p;
+        p.w = w;
+        p.status = TPL_E_ARG;
+        p.reason = "a swizzle needs 0 <= bits <= 16, base >= 0, shift >= bits and base + shift + bits <= 48";
+        return p;
+    }
+    const int lw = (w == 1 || w == 2 || w == 4 || w == 8 || w == 16) ? log2_width(w) : 0;
+    const int64_t big = (int64_t)1 << 30;
+    const int64_t gs = zs.bits ? ((int64_t)1 << std::min(30, zs.base + lw)) : big;
+    const int64_t gd = zd.bits ? ((int64_t)1 << std::min(30, zd.base + lw)) : big;
+    Plan p = plan_core(w, rank, ext, ss, ds, offs, batch, src_align, dst_align, gs, gd);
+    p.zs = zs;
+    p.zd = zd;
+    if (p.status != TPL_OK) return p;
+    const Swz bs = swz_bytes(zs, w), bd = swz_bytes(zd, w);
+    p.gather.zs = p.copy.zs = p.quad.zs = p.lds.zs = bs;
+    p.gather.zd = p.copy.zd = p.quad.zd = p.lds.zd = bd;
+    // Swizzled offsets reach up to (plain offset | mask): 64-bit index math
+    // when that passes 2^31 elements.
+    if (zs.bits || zd.bits) {
+        int64_t mx = 0;
+        for (int i = 0; i < p.shard.rank; ++i)
+            mx = std::max(mx, (p.shard.m[i].e - 1) * std::max(p.shard.m[i].s, p.shard.m[i].d));
+        const int64_t m = (((int64_t)1 << std::max(zs.bits, zd.bits)) - 1) << std::max(zs.base, zd.base);
+        if ((mx | m) >= ((int64_t)1 << 31) || mx + m >= ((int64_t)1 << 31)) p.big = true;
+    }
+    return p;
+}
+
 // Overlap is allowed unit-for-unit: every batch item is moved by one work
 // unit that reads all before writing (the planner's unit_is_item), items sit
 // at the same offsets on both sides and do not overlap each other, and an
@@ -679,15 +752,28 @@ const LdsShape* swap_shapes(int* n) {
 }
 
 Plan plan_inplace(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                  const int64_t* offs, int64_t batch, int src_align, int dst_align) {
-    Plan p = plan_gfx950(w, rank, ext, ss, ds, offs, batch, src_align, dst_align);
-    if (p.status != TPL_OK || p.kernel == TPL_KERNEL_NONE || inplace_by_unit(p)) return p;
+                  const int64_t* offs, int64_t batch, int src_align, int dst_align, const SwzSpec& zs,
+                  const SwzSpec& zd) {
+    Plan p = plan_gfx950(w, rank, ext, ss, ds, offs, batch, src_align, dst_align, zs, zd);
     auto decline = [&](const char* why) {
         p.status = TPL_E_ALIAS;
         p.reason = std::string("source and destination are the same memory: ") + why;
         p.kernel = TPL_KERNEL_NONE;
         return p;
     };
+    if (p.status != TPL_OK || p.kernel == TPL_KERNEL_NONE) return p;
+    if (zs.bits || zd.bits) {
+        const bool same = zs.bits == zd.bits && (zs.bits == 0 || (zs.base == zd.base && zs.shift == zd.shift));
+        bool identity = same;
+        for (int i = 0; i < p.shard.rank; ++i) identity = identity && p.shard.m[i].s == p.shard.m[i].d;
+        if (identity && p.src_off_bytes == p.dst_off_bytes) {
+            p.kernel = TPL_KERNEL_NONE;
+            p.grid = p.block = 0;
+            return p;
+        }
+        return decline("swizzled operands are not permuted in place");
+    }
+    if (inplace_by_unit(p)) return p;
     if (p.src_off_bytes != p.dst_off_bytes) return decline("offsets differ");
     const Shard& sh = p.shard;
     bool identity = true;

@@ -41,8 +41,19 @@ const Geometry& geometry_gfx950();
 bool step_conflict_free(const Geometry& g, bool is_write, int bytes, const int64_t* addr,
                         const bool* active, int lanes);
 
+// An operand swizzle as the caller gives it, in elements: bits [base,
+// base + bits) of the layout offset are XORed with bits [base + shift,
+// base + shift + bits).  bits == 0: plain layout.
+struct SwzSpec {
+    int bits = 0, base = 0, shift = 0;
+};
+
+bool swz_valid(const SwzSpec& z);
+Swz swz_bytes(const SwzSpec& z, int w);   // the same swizzle on byte offsets
+
 struct Plan {
     int status = TPL_OK;
+    SwzSpec zs, zd;         // operand swizzles
     std::string reason;
     Shard shard;            // canonical shard, batch folded in
     int w = 0;
@@ -69,13 +80,15 @@ struct Plan {
 // Full planning for the device path.  src_align / dst_align: alignment in
 // bytes of the base pointers (after elem_offsets are applied).
 Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                 const int64_t* offs, int64_t batch, int src_align, int dst_align);
+                 const int64_t* offs, int64_t batch, int src_align, int dst_align,
+                 const SwzSpec& zs = SwzSpec(), const SwzSpec& zd = SwzSpec());
 
 // The plan for src == dst: the device plan when each of its work units reads
 // its whole footprint before writing it; else the pair-swap plan of a square
 // transpose; else TPL_E_ALIAS.
 Plan plan_inplace(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                  const int64_t* offs, int64_t batch, int src_align, int dst_align);
+                  const int64_t* offs, int64_t batch, int src_align, int dst_align,
+                  const SwzSpec& zs = SwzSpec(), const SwzSpec& zd = SwzSpec());
 
 // Does the device plan move every batch item with one read-before-write unit,
 // so that it may run with src == dst?
@@ -85,15 +98,15 @@ const LdsShape* swap_shapes(int* n);
 
 // The pages' method on one warp region (32 lanes, 32 banks).
 Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                  int64_t batch);
+                  int64_t batch, const SwzSpec& zs = SwzSpec(), const SwzSpec& zd = SwzSpec());
 
 // The same 32-lane program run by one gfx950 half-wave on LDS, with the
 // measured gfx950 bank model.
 Plan plan_halfwave(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
-                   int64_t batch);
+                   int64_t batch, const SwzSpec& zs = SwzSpec(), const SwzSpec& zd = SwzSpec());
 
 Plan plan_warp32(const Geometry& g, int w, int rank, const int64_t* ext, const int64_t* ss,
-                 const int64_t* ds, int64_t batch);
+                 const int64_t* ds, int64_t batch, const SwzSpec& zs = SwzSpec(), const SwzSpec& zd = SwzSpec());
 
 // Canonical shard (unit modes dropped, neighbours merged where both sides merge).
 Shard make_shard(int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,

@@ -28,6 +28,7 @@ struct StagedArgs {
     int32_t vec;                // copy vector: 16, 4 or 1 bytes
     int32_t shift, mask;
     tpl_wave::Shard sh;
+    tpl_wave::Swizzle zs, zd;
 };
 
 template <int V> struct CopyT;
@@ -59,7 +60,7 @@ __global__ void __launch_bounds__(64) k_staged(StagedArgs a) {
     if (act) group_copy_v(ls, a.src + item * a.span_s, a.src_bytes, lane, a.vec);
     __syncthreads();
     if (act) tpl_wave::group_permute<T, P>(reinterpret_cast<T*>(ld), reinterpret_cast<const T*>(ls), a.sh, lane,
-                                           a.shift, a.mask);
+                                           a.shift, a.mask, a.zs, a.zd);
     __syncthreads();
     if (act) group_copy_v(a.dst + item * a.span_d, ld, a.dst_bytes, lane, a.vec);
 }
@@ -83,8 +84,28 @@ static int align_of(uintptr_t x) {
     return a;
 }
 
+static SwzSpec staged_spec(const tpl_swizzle* z) {
+    SwzSpec s;
+    if (z) {
+        s.bits = z->bits;
+        s.base = z->base;
+        s.shift = z->shift;
+    }
+    return s;
+}
+
+static int64_t swz_of(const SwzSpec& z, int64_t m) {
+    if (z.bits == 0) return m;
+    return m ^ (((m >> (z.base + z.shift)) & (((int64_t)1 << z.bits) - 1)) << z.base);
+}
+
 static int staged_impl(const void* src, void* dst, int w, int rank, const int64_t* ext, const int64_t* ss,
-                       const int64_t* ds, const int64_t* offs_in, int64_t batch, int xor_k, hipStream_t stream) {
+                       const int64_t* ds, const int64_t* offs_in, int64_t batch, const tpl_swizzle* zs_in,
+                       const tpl_swizzle* zd_in, int xor_k, hipStream_t stream) {
+    const SwzSpec zs = staged_spec(zs_in), zd = staged_spec(zd_in);
+    if (!swz_valid(zs) || !swz_valid(zd))
+        return fail_status(TPL_E_ARG,
+                           "a swizzle needs 0 <= bits <= 16, base >= 0, shift >= bits, base + shift + bits <= 48");
     if (rank < 1 || rank > TPL_MAX_RANK || !ext || !ss || !ds) return fail_status(TPL_E_ARG, "rank must be in 1..8");
     if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16)
         return fail_status(TPL_E_DTYPE_WIDTH, "unsupported dtype byte width (must be 1, 2, 4, 8 or 16)");
@@ -101,7 +122,7 @@ static int staged_impl(const void* src, void* dst, int w, int rank, const int64_
     if (offs[0] < 0 || offs[1] < 0) return fail_status(TPL_E_LAYOUT, "layouts must slice/canonicalize: negative offsets");
 
     // The per-item program: the pages' warp plan on the half-wave bank model.
-    Plan p = plan_halfwave(w, rank, ext, ss, ds, 1);
+    Plan p = plan_halfwave(w, rank, ext, ss, ds, 1, zs, zd);
     if (p.status != TPL_OK && p.status != TPL_E_NO_K) return fail_status(p.status, p.reason);
     const int64_t P = p.P;
     if (P < 1 || P > 32 || (P & (P - 1)))
@@ -115,6 +136,24 @@ static int staged_impl(const void* src, void* dst, int w, int rank, const int64_
     if (cos_d != prod) return fail_status(TPL_E_LAYOUT, "staged permute needs a dense destination footprint");
     if (cos_s * w > 8192 || cos_d * w > 8192)
         return fail_status(TPL_E_LAYOUT, "staged permute footprints must fit 8 KiB");
+    // Swizzled sides: every swizzled offset of an item stays inside the item's
+    // footprint [0, span) (a bijection of it, so the destination stays
+    // dense), and with several items the span is a multiple of the swizzle
+    // period, so that item b's offsets are b * span plus those of item 0.
+    for (int side = 0; side < 2; ++side) {
+        const SwzSpec& z = side ? zd : zs;
+        if (z.bits == 0) continue;
+        const int64_t span = side ? cos_d : cos_s;
+        const int64_t period = (int64_t)1 << (z.base + z.shift + z.bits);
+        if (batch > 1 && span % period != 0)
+            return fail_status(TPL_E_LAYOUT, "staged permute: with batch > 1 a swizzled side's item span must be "
+                                             "a multiple of the swizzle period");
+        for (int64_t m = 0; m < span; ++m)
+            if (swz_of(z, m) >= span)
+                return fail_status(TPL_E_LAYOUT, "staged permute: the swizzle leaves the item footprint");
+    }
+    const tpl_wave::Swizzle wzs{zs.bits ? (int)((((int64_t)1 << zs.bits) - 1) << zs.base) : 0, zs.shift};
+    const tpl_wave::Swizzle wzd{zd.bits ? (int)((((int64_t)1 << zd.bits) - 1) << zd.base) : 0, zd.shift};
     int shift = p.shift, mask = p.mask;
     if (xor_k >= 0) {
         if ((1ll << xor_k) > P || xor_k > 5) return fail_status(TPL_E_ARG, "forced k exceeds log2(P)");
@@ -149,6 +188,8 @@ static int staged_impl(const void* src, void* dst, int w, int rank, const int64_
     a.vec = vec;
     a.shift = shift;
     a.mask = mask;
+    a.zs = wzs;
+    a.zd = wzd;
     a.sh.rank = p.shard.rank;
     for (int i = 0; i < p.shard.rank; ++i) {
         a.sh.extent[i] = (int)p.shard.m[i].e;
@@ -175,10 +216,11 @@ static int staged_impl(const void* src, void* dst, int w, int rank, const int64_
 
 extern "C" int tpl_permute_staged(const void* src, void* dst, int dtype_bytes, int rank, const int64_t* extents,
                                   const int64_t* src_strides, const int64_t* dst_strides,
-                                  const int64_t* elem_offsets, int64_t batch, int xor_k, hipStream_t stream) {
+                                  const int64_t* elem_offsets, int64_t batch, const tpl_swizzle* src_swizzle,
+                                  const tpl_swizzle* dst_swizzle, int xor_k, hipStream_t stream) {
     try {
         return tpl::staged_impl(src, dst, dtype_bytes, rank, extents, src_strides, dst_strides, elem_offsets, batch,
-                                xor_k, stream);
+                                src_swizzle, dst_swizzle, xor_k, stream);
     } catch (...) {
         return tpl::fail_status(TPL_E_ARG, "internal error");
     }

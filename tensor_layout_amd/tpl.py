@@ -36,13 +36,25 @@ TPL_GEOM_GFX950_INPLACE = 3
 KERNELS = {0: "none", 1: "gather", 2: "quad", 3: "lds", 4: "reg16", 5: "copy", 6: "swap"}
 MAX_SHARD = 10
 
-EXPORTED = ("tpl_permute", "tpl_plan", "tpl_status_string", "tpl_last_error", "tpl_permute_staged")
+EXPORTED = ("tpl_permute", "tpl_plan", "tpl_status_string", "tpl_last_error", "tpl_permute_staged",
+            "tpl_permute_swizzled", "tpl_plan_swizzled")
 
 
 class TplError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{message} (status {status})")
         self.status = status
+
+
+class _Swizzle(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("base", ctypes.c_int32), ("shift", ctypes.c_int32)]
+
+
+def _swz(z):
+    """(bits, base, shift) or None -> pointer to a tpl_swizzle (None = plain)."""
+    if z is None:
+        return None
+    return ctypes.byref(_Swizzle(int(z[0]), int(z[1]), int(z[2])))
 
 
 class _PlanInfo(ctypes.Structure):
@@ -118,12 +130,20 @@ def load(path: str = LIB_PATH):
     lib.tpl_permute.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                 i64p, i64p, i64p, i64p, ctypes.c_int64, ctypes.c_void_p]
     lib.tpl_permute.restype = ctypes.c_int
+    zp = ctypes.POINTER(_Swizzle)
+    lib.tpl_permute_swizzled.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                         i64p, i64p, i64p, i64p, ctypes.c_int64, zp, zp, ctypes.c_void_p]
+    lib.tpl_permute_swizzled.restype = ctypes.c_int
     lib.tpl_permute_staged.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                       i64p, i64p, i64p, i64p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+                                       i64p, i64p, i64p, i64p, ctypes.c_int64, zp, zp, ctypes.c_int,
+                                       ctypes.c_void_p]
     lib.tpl_permute_staged.restype = ctypes.c_int
     lib.tpl_plan.argtypes = [ctypes.c_int, ctypes.c_int, i64p, i64p, i64p, i64p, ctypes.c_int64,
                              ctypes.c_int, ctypes.POINTER(_PlanInfo)]
     lib.tpl_plan.restype = ctypes.c_int
+    lib.tpl_plan_swizzled.argtypes = [ctypes.c_int, ctypes.c_int, i64p, i64p, i64p, i64p, ctypes.c_int64,
+                                      zp, zp, ctypes.c_int, ctypes.POINTER(_PlanInfo)]
+    lib.tpl_plan_swizzled.restype = ctypes.c_int
     lib.tpl_status_string.argtypes = [ctypes.c_int]
     lib.tpl_status_string.restype = ctypes.c_char_p
     lib.tpl_last_error.argtypes = []
@@ -154,8 +174,20 @@ def tpl_permute(src_ptr: int, dst_ptr: int, dtype_bytes: int, extents: Sequence[
                            _arr(elem_offsets), int(batch), ctypes.c_void_p(stream))
 
 
+def tpl_permute_swizzled(src_ptr: int, dst_ptr: int, dtype_bytes: int, extents: Sequence[int],
+                         src_strides: Sequence[int], dst_strides: Sequence[int],
+                         elem_offsets: Sequence[int] = (0, 0), batch: int = 1, src_swizzle=None,
+                         dst_swizzle=None, stream: int = 0) -> int:
+    """tpl_permute with swizzled operands; a swizzle is (bits, base, shift) or None."""
+    lib = load()
+    return lib.tpl_permute_swizzled(ctypes.c_void_p(src_ptr), ctypes.c_void_p(dst_ptr), int(dtype_bytes),
+                                    len(extents), _arr(extents), _arr(src_strides), _arr(dst_strides),
+                                    _arr(elem_offsets), int(batch), _swz(src_swizzle), _swz(dst_swizzle),
+                                    ctypes.c_void_p(stream))
+
+
 class PreparedPermute:
-    """tpl_permute with the layout arguments marshalled once.
+    """tpl_permute (or tpl_permute_swizzled) with the layout arguments marshalled once.
 
     Calling the object with (src_ptr, dst_ptr, stream) makes the same C call
     as tpl_permute(src_ptr, dst_ptr, dtype_bytes, extents, ...), without
@@ -163,36 +195,53 @@ class PreparedPermute:
     """
 
     def __init__(self, dtype_bytes: int, extents: Sequence[int], src_strides: Sequence[int],
-                 dst_strides: Sequence[int], elem_offsets: Sequence[int] = (0, 0), batch: int = 1):
-        self._fn = load().tpl_permute
+                 dst_strides: Sequence[int], elem_offsets: Sequence[int] = (0, 0), batch: int = 1,
+                 src_swizzle=None, dst_swizzle=None):
+        lib = load()
         self._args = (int(dtype_bytes), len(extents), _arr(extents), _arr(src_strides), _arr(dst_strides),
                       _arr(elem_offsets), int(batch))
+        if src_swizzle is None and dst_swizzle is None:
+            self._fn = lib.tpl_permute
+            self._swz = ()
+        else:
+            self._fn = lib.tpl_permute_swizzled
+            self._zs = _Swizzle(*src_swizzle) if src_swizzle is not None else None
+            self._zd = _Swizzle(*dst_swizzle) if dst_swizzle is not None else None
+            self._swz = (ctypes.byref(self._zs) if self._zs is not None else None,
+                         ctypes.byref(self._zd) if self._zd is not None else None)
 
     def __call__(self, src_ptr: int, dst_ptr: int, stream: int = 0) -> int:
         w, rank, e, s, d, o, b = self._args
-        return self._fn(src_ptr, dst_ptr, w, rank, e, s, d, o, b, stream)
+        return self._fn(src_ptr, dst_ptr, w, rank, e, s, d, o, b, *self._swz, stream)
 
 
 def tpl_permute_staged(src_ptr: int, dst_ptr: int, dtype_bytes: int, extents: Sequence[int],
                        src_strides: Sequence[int], dst_strides: Sequence[int],
                        elem_offsets: Sequence[int] = (0, 0), batch: int = 1, xor_k: int = -1,
-                       stream: int = 0) -> int:
+                       stream: int = 0, src_swizzle=None, dst_swizzle=None) -> int:
     """Call the staged (one batch item per half-wave, through LDS) entry point."""
     lib = load()
     return lib.tpl_permute_staged(ctypes.c_void_p(src_ptr), ctypes.c_void_p(dst_ptr), int(dtype_bytes),
                                   len(extents), _arr(extents), _arr(src_strides), _arr(dst_strides),
-                                  _arr(elem_offsets), int(batch), int(xor_k), ctypes.c_void_p(stream))
+                                  _arr(elem_offsets), int(batch), _swz(src_swizzle), _swz(dst_swizzle),
+                                  int(xor_k), ctypes.c_void_p(stream))
 
 
 def tpl_plan(dtype_bytes: int, extents: Sequence[int], src_strides: Sequence[int],
              dst_strides: Sequence[int], elem_offsets: Optional[Sequence[int]] = None,
-             batch: int = 1, geometry: int = TPL_GEOM_GFX950) -> PlanInfo:
-    """Host-only planning (no GPU needed)."""
+             batch: int = 1, geometry: int = TPL_GEOM_GFX950, src_swizzle=None,
+             dst_swizzle=None) -> PlanInfo:
+    """Host-only planning (no GPU needed); with swizzles it calls tpl_plan_swizzled."""
     lib = load()
     info = _PlanInfo()
     offs = _arr(elem_offsets) if elem_offsets is not None else None
-    st = lib.tpl_plan(int(dtype_bytes), len(extents), _arr(extents), _arr(src_strides),
-                      _arr(dst_strides), offs, int(batch), int(geometry), ctypes.byref(info))
+    if src_swizzle is None and dst_swizzle is None:
+        st = lib.tpl_plan(int(dtype_bytes), len(extents), _arr(extents), _arr(src_strides),
+                          _arr(dst_strides), offs, int(batch), int(geometry), ctypes.byref(info))
+    else:
+        st = lib.tpl_plan_swizzled(int(dtype_bytes), len(extents), _arr(extents), _arr(src_strides),
+                                   _arr(dst_strides), offs, int(batch), _swz(src_swizzle), _swz(dst_swizzle),
+                                   int(geometry), ctypes.byref(info))
     reason = tpl_last_error() if st != TPL_OK else ""
     r = info.rank
     return PlanInfo(st, reason, list(info.extent[:r]), list(info.src_str[:r]), list(info.dst_str[:r]),
@@ -208,9 +257,16 @@ def _cosize(extents, strides):
     return 1 + sum((e - 1) * s for e, s in zip(extents, strides))
 
 
+def _swz_reach(n_elems, z):
+    """One past the largest swizzled offset of offsets 0 .. n_elems - 1 (bound)."""
+    if z is None or z[0] == 0 or n_elems == 0:
+        return n_elems
+    return ((n_elems - 1) | (((1 << z[0]) - 1) << z[1])) + 1
+
+
 def permute(dst, src, extents: Sequence[int], src_strides: Sequence[int], dst_strides: Sequence[int],
             src_offset: int = 0, dst_offset: int = 0, batch: int = 1, dtype_bytes: Optional[int] = None,
-            stream=None) -> None:
+            stream=None, src_swizzle=None, dst_swizzle=None) -> None:
     """Permute ``src`` into ``dst`` (torch tensors on the GPU, used as flat storage).
 
     Argument order is (dst, src) as in the pages' ``permute_layout(dst, src)``.
@@ -232,14 +288,18 @@ def permute(dst, src, extents: Sequence[int], src_strides: Sequence[int], dst_st
     for e in extents:
         n *= e
     if n > 0:
-        need_s = (src_offset + batch * _cosize(extents, src_strides)) * w
-        need_d = (dst_offset + batch * _cosize(extents, dst_strides)) * w
+        need_s = (src_offset + _swz_reach(batch * _cosize(extents, src_strides), src_swizzle)) * w
+        need_d = (dst_offset + _swz_reach(batch * _cosize(extents, dst_strides), dst_swizzle)) * w
         if need_s > src.numel() * src.element_size() or need_d > dst.numel() * dst.element_size():
             raise TplError(TPL_E_ARG, "layout reaches past the end of a tensor")
     if stream is None:
         stream = torch.cuda.current_stream(src.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    st = tpl_permute(src.data_ptr(), dst.data_ptr(), w, extents, src_strides, dst_strides,
-                     (src_offset, dst_offset), batch, sp)
+    if src_swizzle is None and dst_swizzle is None:
+        st = tpl_permute(src.data_ptr(), dst.data_ptr(), w, extents, src_strides, dst_strides,
+                         (src_offset, dst_offset), batch, sp)
+    else:
+        st = tpl_permute_swizzled(src.data_ptr(), dst.data_ptr(), w, extents, src_strides, dst_strides,
+                                  (src_offset, dst_offset), batch, src_swizzle, dst_swizzle, sp)
     if st != TPL_OK:
         raise TplError(st, tpl_last_error())

@@ -9,7 +9,7 @@ number + sub-case.  Nothing here computes an address.
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Tuple
+from typing import Optional, Tuple
 
 
 @dataclass(frozen=True)
@@ -24,6 +24,8 @@ class Workload:
     seed: int = 0
     specials: bool = False   # force fp32 special encodings into the input
     inplace: bool = False    # source and destination are one buffer
+    src_swizzle: Optional[Tuple[int, int, int]] = None   # (bits, base, shift) or None
+    dst_swizzle: Optional[Tuple[int, int, int]] = None
 
     @property
     def elements(self) -> int:
@@ -74,6 +76,15 @@ W16_4K = Workload("transpose_4096x4096_16B", 16, (4096, 4096), (4096, 1), (1, 40
 OUTER_PERM = Workload("axes1023_64x128x32x32_f32_runs", 4, (64, 128, 32, 32),
                       (131072, 1024, 32, 1), (1024, 65536, 32, 1), seed=_seed(6))
 
+# The SF transpose into XOR-swizzled destination tiles: the 16-byte chunk
+# index of each 128-element tile (bits 2..3 of the offset) is XORed with bits
+# 5..6; the swizzle period is one tile.
+SF_SWIZZLED = Workload("sf_transpose_2^20x4x32_f32_to_swizzled", 4, (4, 32), (32, 1), (1, 4),
+                       batch=1 << 20, seed=_seed(2, 1), specials=True, dst_swizzle=(2, 2, 3))
+# The fp16 tiles into MMA-style swizzled column-major tiles: 16-byte chunks of
+# each 256-byte destination row XORed with the row index (bits 3..5 ^= 7..9).
+TILE_SWIZZLED = Workload("tile_65536x128x64_f16_to_swizzled_colmajor", 2, (128, 64), (64, 1), (1, 128),
+                         batch=65536, seed=_seed(3, 1), dst_swizzle=(3, 3, 4))
 # The 16384^2 bf16 transpose with source and destination in one buffer.
 BF16_16K_INPLACE = Workload("transpose_16384x16384_bf16_inplace", 2, (16384, 16384), (16384, 1), (1, 16384),
                             seed=_seed(5, 2), inplace=True)
@@ -81,7 +92,8 @@ BF16_16K_INPLACE = Workload("transpose_16384x16384_bf16_inplace", 2, (16384, 163
 # size, used to calibrate the HBM byte counters.
 COPY_CALIBRATION = Workload("identity_copy_512MiB_u32", 4, (1 << 27,), (1,), (1,), seed=0x5EED0100)
 
-ALL = [SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)] + [BF16_16K, W16_4K, OUTER_PERM]
+ALL = ([SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)]
+       + [BF16_16K, W16_4K, OUTER_PERM, SF_SWIZZLED, TILE_SWIZZLED])
 INPLACE = [BF16_16K_INPLACE]
 
 

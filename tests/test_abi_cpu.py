@@ -149,12 +149,15 @@ EXPECTED_KERNEL = {
     "transpose_16384x16384_bf16": "lds",
     "transpose_4096x4096_16B": "lds",
     "axes1023_64x128x32x32_f32_runs": "copy",
+    "sf_transpose_2^20x4x32_f32_to_swizzled": "quad",
+    "tile_65536x128x64_f16_to_swizzled_colmajor": "lds",
 }
 
 
 @pytest.mark.parametrize("wl", workloads.ALL, ids=lambda w: w.name)
 def test_gfx950_kernel_choice(wl):
-    p = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, batch=wl.batch)
+    p = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, batch=wl.batch,
+                     src_swizzle=wl.src_swizzle, dst_swizzle=wl.dst_swizzle)
     assert p.ok, p.reason
     assert p.kernel == EXPECTED_KERNEL[wl.name]
 
@@ -366,3 +369,95 @@ def test_inplace_unaligned_bases_use_element_path_or_decline():
     # 8-byte elements at a 4-byte aligned base are still fine (4-byte pieces)
     p = tpl.tpl_plan(8, (100, 100), (100, 1), (1, 100), (0, 0), geometry=G_IN)
     assert p.ok
+
+
+# ---------------------------------------------------------------------------
+# swizzled operands
+
+
+def _swizzle_family():
+    rng = np.random.default_rng(77)
+    out = []
+    for w, ext, ss, ds in _family()[::3]:
+        for _ in range(2):
+            def one():
+                if rng.random() < 0.3:
+                    return None
+                bits = int(rng.integers(1, 4))
+                return (bits, int(rng.integers(0, 3)), int(rng.integers(bits, 5)))
+            out.append((w, ext, ss, ds, one(), one()))
+    return out
+
+
+def test_pages32_swizzled_agrees_with_plan_oracle():
+    n_ok = 0
+    for w, ext, ss, ds, zs, zd in _swizzle_family():
+        o = po.plan(w, ext, ss, ds, src_swz=zs, dst_swz=zd)
+        p = tpl.tpl_plan(w, ext, ss, ds, geometry=tpl.TPL_GEOM_PAGES32, src_swizzle=zs or (0, 0, 0),
+                         dst_swizzle=zd)
+        assert p.ok == o.ok, (w, ext, ss, ds, zs, zd, o, p)
+        if o.ok:
+            n_ok += 1
+            assert (p.P, p.k, p.shift, p.mask) == (o.P, o.k, o.shift, o.mask), (w, ext, ss, ds, zs, zd)
+    assert n_ok > 30
+
+
+def test_pages32_swizzled_transpose_needs_no_xor():
+    p = tpl.tpl_plan(4, (32, 32), (32, 1), (1, 32), geometry=tpl.TPL_GEOM_PAGES32)
+    q = tpl.tpl_plan(4, (32, 32), (32, 1), (1, 32), geometry=tpl.TPL_GEOM_PAGES32, dst_swizzle=(5, 0, 5))
+    assert (p.k, q.k) == (5, 0)
+    h = tpl.tpl_plan(4, (32, 32), (32, 1), (1, 32), geometry=tpl.TPL_GEOM_GFX950_HALFWAVE, dst_swizzle=(5, 0, 5))
+    assert h.ok and h.k == 0
+
+
+@pytest.mark.parametrize("w,ext,ss,ds,zs,zd,kernel", [
+    # SF tiles into a destination swizzled on 16-byte granules: the quad kernel
+    (4, (4, 32), (32, 1), (1, 4), None, (3, 2, 3), "quad"),
+    (4, (4, 32), (32, 1), (1, 4), (2, 2, 3), None, "quad"),
+    # 8-byte granules: element-wise
+    (4, (4, 32), (32, 1), (1, 4), None, (3, 1, 3), "gather"),
+    # fp16 tiles into an MMA-style swizzled column-major tile (16-byte chunks)
+    (2, (128, 64), (64, 1), (1, 128), None, (3, 3, 4), "lds"),
+    (1, (256, 256), (256, 1), (1, 256), (3, 4, 4), (3, 4, 5), "lds"),
+    (8, (64, 64), (64, 1), (1, 64), (2, 1, 3), None, "lds"),
+    # 16-byte elements: every element is a granule; small shapes take the LDS
+    # kernel's ragged (element-wise) tile instead of the plain-only 8x8 remap
+    (16, (64, 64), (64, 1), (1, 64), (3, 0, 3), (3, 0, 6), "lds"),
+    (16, (8, 8), (8, 1), (1, 8), None, (3, 0, 3), "lds"),
+    # runs copied in vectors no wider than the granule
+    (4, (64, 64), (64, 1), (64, 1), None, (2, 1, 4), "copy"),
+])
+def test_swizzled_kernel_selection(w, ext, ss, ds, zs, zd, kernel):
+    p = tpl.tpl_plan(w, ext, ss, ds, batch=8, src_swizzle=zs, dst_swizzle=zd)
+    assert p.ok and p.kernel == kernel, p
+
+
+@pytest.mark.parametrize("z", [(2, 0, 1), (-1, 0, 0), (1, -1, 1), (17, 0, 17), (8, 20, 30)])
+def test_invalid_swizzle_is_refused(z):
+    p = tpl.tpl_plan(4, (4, 32), (32, 1), (1, 4), dst_swizzle=z)
+    assert p.status == tpl.TPL_E_ARG
+    sp = 1 << 20
+    assert tpl.tpl_permute_swizzled(sp, sp + (1 << 20), 4, (4, 32), (32, 1), (1, 4), (0, 0), 1, None, z) \
+        == tpl.TPL_E_ARG
+
+
+def test_swizzled_in_place():
+    G_IN = tpl.TPL_GEOM_GFX950_INPLACE
+    p = tpl.tpl_plan(2, (64, 64), (64, 1), (1, 64), geometry=G_IN, dst_swizzle=(3, 3, 3))
+    assert p.status == tpl.TPL_E_ALIAS
+    q = tpl.tpl_plan(2, (64, 64), (64, 1), (64, 1), geometry=G_IN, src_swizzle=(3, 3, 3), dst_swizzle=(3, 3, 3))
+    assert q.ok and q.kernel == "none"
+
+
+def test_swizzled_staged_declines_on_the_host():
+    sp, dp = 1 << 20, 1 << 24   # never dereferenced: every call below declines
+    # source rows padded to 40: the 152-element footprint is not closed under
+    # the swizzle (2, 3, 3) (offset 140 goes to 156)
+    assert tpl.tpl_permute_staged(sp, dp, 4, (4, 32), (40, 1), (1, 4), (0, 0), 1, -1, 0, (2, 3, 3), None) \
+        == tpl.TPL_E_LAYOUT
+    # batch > 1 with an item span (128) that is not a multiple of the period 2^(2+4+2)
+    assert tpl.tpl_permute_staged(sp, dp, 4, (4, 32), (32, 1), (1, 4), (0, 0), 4, -1, 0, None, (2, 2, 4)) \
+        == tpl.TPL_E_LAYOUT
+    # an invalid swizzle
+    assert tpl.tpl_permute_staged(sp, dp, 4, (4, 32), (32, 1), (1, 4), (0, 0), 4, -1, 0, None, (3, 0, 2)) \
+        == tpl.TPL_E_ARG

@@ -33,9 +33,9 @@ def cosize(extents, strides):
     return 1 + sum((e - 1) * s for e, s in zip(extents, strides))
 
 
-def sizes(w, ext, ss, ds, offs, batch):
-    ns = offs[0] + batch * cosize(ext, ss)
-    nd = offs[1] + batch * cosize(ext, ds)
+def sizes(w, ext, ss, ds, offs, batch, zs=None, zd=None):
+    ns = offs[0] + tpl._swz_reach(batch * cosize(ext, ss), zs)
+    nd = offs[1] + tpl._swz_reach(batch * cosize(ext, ds), zd)
     return ns * w, nd * w
 
 
@@ -46,20 +46,21 @@ def make_input(seed, nbytes, specials=False, w=4):
     return x
 
 
-def run_case(name, w, ext, ss, ds, offs=(0, 0), batch=1, seed=1, specials=False, expect_kernel=None):
+def run_case(name, w, ext, ss, ds, offs=(0, 0), batch=1, seed=1, specials=False, expect_kernel=None,
+             zs=None, zd=None):
     torch = _torch()
-    print(f"\n[case] {name}: w={w} ext={tuple(ext)} ss={tuple(ss)} ds={tuple(ds)} offs={tuple(offs)} batch={batch}",
-          flush=True)
-    nbs, nbd = sizes(w, ext, ss, ds, offs, batch)
+    print(f"\n[case] {name}: w={w} ext={tuple(ext)} ss={tuple(ss)} ds={tuple(ds)} offs={tuple(offs)} batch={batch}"
+          f" swizzles={zs},{zd}", flush=True)
+    nbs, nbd = sizes(w, ext, ss, ds, offs, batch, zs, zd)
     x = make_input(seed, nbs, specials, w)
     ref = np.full(nbd, SENTINEL, dtype=np.uint8)
-    oracle.permute(x, ref, w, ext, ss, ds, offs, batch)
+    oracle.permute(x, ref, w, ext, ss, ds, offs, batch, zs, zd)
     s = torch.from_numpy(x).cuda()
     d = torch.full((max(nbd, 1),), SENTINEL, dtype=torch.uint8, device="cuda")
     if expect_kernel is not None:
-        plan = tpl.tpl_plan(w, ext, ss, ds, offs, batch)
+        plan = tpl.tpl_plan(w, ext, ss, ds, offs, batch, src_swizzle=zs, dst_swizzle=zd)
         assert plan.kernel == expect_kernel, plan
-    tpl.permute(d, s, ext, ss, ds, offs[0], offs[1], batch, dtype_bytes=w)
+    tpl.permute(d, s, ext, ss, ds, offs[0], offs[1], batch, dtype_bytes=w, src_swizzle=zs, dst_swizzle=zd)
     torch.cuda.synchronize()
     got = d.cpu().numpy()[:nbd]
     if not np.array_equal(got, ref):
@@ -82,13 +83,15 @@ SMALL = [
     workloads.scaled(workloads.mixed_width(8), extents=(2, 128, 32, 32)),
     workloads.Workload("transpose_1024x768_bf16", 2, (1024, 768), (768, 1), (1, 1024), seed=0x5EED0050),
     workloads.Workload("transpose_256x192_16B", 16, (256, 192), (192, 1), (1, 256), seed=0x5EED0051),
+    workloads.scaled(workloads.SF_SWIZZLED, batch=4097),
+    workloads.scaled(workloads.TILE_SWIZZLED, batch=33),
 ]
 
 
 @pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
 def test_workload_small(wl):
     run_case(wl.name, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
-             wl.seed, wl.specials)
+             wl.seed, wl.specials, zs=wl.src_swizzle, zd=wl.dst_swizzle)
 
 
 # ---------------------------------------------------------------------------
@@ -98,7 +101,7 @@ def test_workload_small(wl):
 @pytest.mark.parametrize("wl", workloads.ALL, ids=lambda w: w.name)
 def test_workload_full_size(wl):
     run_case(wl.name, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
-             wl.seed, wl.specials)
+             wl.seed, wl.specials, zs=wl.src_swizzle, zd=wl.dst_swizzle)
 
 
 # ---------------------------------------------------------------------------
