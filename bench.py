@@ -96,7 +96,7 @@ def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
     }, y
 
 
-def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
+def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, do_ceiling=True):
     import numpy as np
     import torch
     from tensor_layout_amd import tpl
@@ -162,8 +162,9 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
     value = wl.bytes_moved * steps / elapsed / 1e9
     achieved = wl.bytes_moved / (avg_ms * 1e-3) / 1e9
 
+
     out = {
-        "metric": METRIC if wl.name.startswith("sf_transpose") else f"permute_layout GB/s (rd+wr), {wl.name}",
+        "metric": METRIC if wl.name == "sf_transpose_2^20x4x32_f32" else f"permute_layout GB/s (rd+wr), {wl.name}",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -219,6 +220,26 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1):
             last = (warmup + steps - 1) % pairs
             got = dsts[last].cpu().numpy()
         out["bitexact"] = bool(np.array_equal(got, ref))
+    # Reference, after the check (it overwrites the outputs): a plain copy of
+    # the same bytes (the library's identity-layout copy, 16-byte vectors)
+    # over the same buffer rotation, timed the same way.
+    ceiling = None
+    if do_ceiling and nbytes % 16 == 0 and entry == "permute":
+        ident = tpl.PreparedPermute(16, (nbytes // 16,), (1,), (1,))
+        cptrs = [(srcs[i].data_ptr(), (srcs[(i + 1) % pairs] if wl.inplace else dsts[i]).data_ptr())
+                 for i in range(pairs)]
+        csteps = min(steps, 200)
+        for i in range(10):
+            ident(*cptrs[i % pairs], sp)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(csteps):
+            ident(*cptrs[i % pairs], sp)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ceiling = 2 * nbytes / (ev0.elapsed_time(ev1) / csteps * 1e-3) / 1e9
+    out["roofline"]["copy_ceiling_gbps"] = round(ceiling, 2) if ceiling else None
+    out["roofline"]["frac_of_copy_ceiling"] = round(achieved / ceiling, 4) if ceiling else None
     del srcs, dsts
     torch.cuda.empty_cache()
     return out
@@ -235,6 +256,8 @@ def main():
                     help="with --all: also run the 512 MiB identity copy used to scale HBM counters")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the plain-copy reference (keeps profiler traces to the permute kernels)")
     ap.add_argument("--entry", choices=("permute", "staged"), default="permute",
                     help="tpl_permute (default) or the half-wave LDS-staged tpl_permute_staged")
     ap.add_argument("--xor-k", type=int, default=-1, help="staged entry: force this XOR k (-1 = planner's)")
@@ -254,11 +277,12 @@ def main():
     if a.all:
         todo = workloads.ALL + workloads.INPLACE + ([workloads.COPY_CALIBRATION] if a.with_calibration else [])
         for wl in todo:
-            print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify)), flush=True)
+            print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify,
+                                       do_ceiling=not a.no_ceiling)), flush=True)
         return
     wl = by_name[a.workload]
-    print(json.dumps(bench_one(wl, a.steps, a.warmup, not a.no_cpu, not a.no_verify, a.entry, a.xor_k)),
-          flush=True)
+    print(json.dumps(bench_one(wl, a.steps, a.warmup, not a.no_cpu, not a.no_verify, a.entry, a.xor_k,
+                               not a.no_ceiling)), flush=True)
 
 
 if __name__ == "__main__":

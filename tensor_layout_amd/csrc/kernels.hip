@@ -531,7 +531,7 @@ static hipError_t launch_lds(const Plan& p, const LdsArgs& a, hipStream_t st) {
     TPL_LDS_SHAPE(4, 32, 32, 2)
     TPL_LDS_SHAPE(8, 32, 64, 2)
     TPL_LDS_SHAPE(8, 16, 32, 2)
-    TPL_LDS_SHAPE(16, 128, 8, 2)
+    TPL_LDS_SHAPE(16, 64, 16, 2)
     TPL_LDS_SHAPE(16, 16, 64, 2)
     TPL_LDS_SHAPE(16, 16, 16, 2)
 #undef TPL_LDS_SHAPE

