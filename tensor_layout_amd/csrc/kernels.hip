@@ -795,11 +795,13 @@ static int64_t cosize_side(const Shard& sh, bool src) {
     return c;
 }
 
-// Bytes from a side's base to one past its last byte: the largest swizzled
-// offset is at most the largest plain byte offset with the swizzle mask set.
+// Bytes from a side's base to one past its last byte.  A swizzle only
+// rewrites the bits below the top of its target field, so no swizzled offset
+// of an offset <= last exceeds last with all those bits set.
 static int64_t reach_bytes(const Plan& p, bool src) {
     const int64_t last = (cosize_side(p.shard, src) - 1) * p.w + (p.w - 1);
-    return (last | swz_bytes(src ? p.zs : p.zd, p.w).ymask) + 1;
+    const int64_t y = swz_bytes(src ? p.zs : p.zd, p.w).ymask;
+    return (y ? (last | y | (y - 1)) : last) + 1;
 }
 
 static SwzSpec spec_of(const tpl_swizzle* z) {

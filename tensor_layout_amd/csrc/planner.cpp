@@ -708,14 +708,16 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
     const Swz bs = swz_bytes(zs, w), bd = swz_bytes(zd, w);
     p.gather.zs = p.copy.zs = p.quad.zs = p.lds.zs = bs;
     p.gather.zd = p.copy.zd = p.quad.zd = p.lds.zd = bd;
-    // Swizzled offsets reach up to (plain offset | mask): 64-bit index math
-    // when that passes 2^31 elements.
+    // A swizzle rewrites only bits below the top of its target field, so a
+    // swizzled offset of an offset <= mx is at most mx with all those bits
+    // set: 64-bit index math when that passes 2^31 elements.
     if (zs.bits || zd.bits) {
         int64_t mx = 0;
-        for (int i = 0; i < p.shard.rank; ++i)
-            mx = std::max(mx, (p.shard.m[i].e - 1) * std::max(p.shard.m[i].s, p.shard.m[i].d));
-        const int64_t m = (((int64_t)1 << std::max(zs.bits, zd.bits)) - 1) << std::max(zs.base, zd.base);
-        if ((mx | m) >= ((int64_t)1 << 31) || mx + m >= ((int64_t)1 << 31)) p.big = true;
+        for (int i = 0; i < p.shard.rank; ++i) {
+            mx += (p.shard.m[i].e - 1) * std::max(p.shard.m[i].s, p.shard.m[i].d);
+        }
+        const int top = std::max(zs.bits ? zs.base + zs.bits : 0, zd.bits ? zd.base + zd.bits : 0);
+        if ((mx | (((int64_t)1 << top) - 1)) >= ((int64_t)1 << 31)) p.big = true;
     }
     return p;
 }

@@ -258,10 +258,11 @@ def _cosize(extents, strides):
 
 
 def _swz_reach(n_elems, z):
-    """One past the largest swizzled offset of offsets 0 .. n_elems - 1 (bound)."""
+    """A bound on one past the largest swizzled offset of offsets 0 .. n_elems - 1:
+    the swizzle rewrites only bits below base + bits."""
     if z is None or z[0] == 0 or n_elems == 0:
         return n_elems
-    return ((n_elems - 1) | (((1 << z[0]) - 1) << z[1])) + 1
+    return ((n_elems - 1) | ((1 << (z[1] + z[0])) - 1)) + 1
 
 
 def permute(dst, src, extents: Sequence[int], src_strides: Sequence[int], dst_strides: Sequence[int],

@@ -461,3 +461,58 @@ def test_swizzled_staged_declines_on_the_host():
     # an invalid swizzle
     assert tpl.tpl_permute_staged(sp, dp, 4, (4, 32), (32, 1), (1, 4), (0, 0), 4, -1, 0, None, (3, 0, 2)) \
         == tpl.TPL_E_ARG
+
+
+def test_planning_is_thread_safe():
+    """Many threads planning different layouts at once (the plan caches are
+    shared; ctypes releases the GIL during each call) get the same plans as
+    one thread does."""
+    import threading
+    cases = [(w, ext, ss, ds) for w, ext, ss, ds in _family()[:120]]
+
+    def plan_all():
+        return [tpl.tpl_plan(w, e, s, d, batch=3) for w, e, s, d in cases]
+
+    want = plan_all()
+    got, errors = [None] * 8, []
+
+    def worker(i):
+        try:
+            for _ in range(5):
+                got[i] = plan_all()
+        except Exception as e:  # pragma: no cover - reported below
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors
+    for g in got:
+        assert g == want
+
+
+def test_swizzle_reach_bound_covers_every_offset():
+    """The binding's buffer-size bound for a swizzled side covers the largest
+    swizzled offset (checked against the oracle's swizzle, exhaustively)."""
+    import oracle
+    for bits in (1, 2, 3):
+        for base in range(4):
+            for shift in range(bits, 6):
+                for n in range(1, 700, 7):
+                    top = max(oracle.swizzle(bits, base, shift, m) for m in range(n))
+                    assert top < tpl._swz_reach(n, (bits, base, shift)), (bits, base, shift, n)
+
+
+def test_swizzled_overlap_uses_the_swizzled_reach():
+    """dst starts right after src's plain footprint, but src's swizzled
+    offsets reach past it: refused before any launch."""
+    sp = 1 << 20   # never dereferenced: the call declines
+    # 40 u32 elements, source swizzled (1, 4, 1) (bit 5 XORed into bit 4):
+    # offset 39 = 0b100111 goes to 0b110111 = 55, past the plain cosize 40.
+    ext, st = (40,), (1,)
+    import oracle
+    assert max(oracle.swizzle(1, 4, 1, m) for m in range(40)) >= 40
+    st_ = tpl.tpl_permute_swizzled(sp, sp + 40 * 4, 4, ext, st, st, (0, 0), 1, (1, 4, 1), None)
+    assert st_ == tpl.TPL_E_ALIAS, tpl.tpl_last_error()

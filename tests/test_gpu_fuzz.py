@@ -1,0 +1,139 @@
+"""Randomised GPU parity: tensor permutations of random shapes, widths,
+offsets, batches and swizzles, sized so that every kernel family is reached,
+each case checked byte for byte against the oracle.  Also: capture in a HIP
+graph and replay, and two streams at once."""
+
+from __future__ import annotations
+
+import collections
+
+import numpy as np
+import pytest
+
+import oracle
+from tensor_layout_amd import synth, tpl
+from tests.test_gpu_parity import run_case, make_input, sizes, SENTINEL
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def random_case(rng, aligned=False):
+    """aligned: 16-byte aligned rows and offsets and swizzle granules of at
+    least 16 bytes, so that the vector kernels take the case."""
+    rank = int(rng.integers(2, 5))
+    w = int(rng.choice([1, 2, 4, 8, 16]))
+    # extents: mostly tile-friendly sizes, some ragged
+    pool = [4, 16, 32, 64, 96, 128] if aligned else [1, 3, 4, 16, 32, 48, 64, 96, 128, 130, 256]
+    ext = [int(rng.choice(pool)) for _ in range(rank)]
+    while int(np.prod(ext)) * w > (4 << 20):
+        ext[int(np.argmax(ext))] //= 2
+    ext = [max(1, e) for e in ext]
+    # source: row-major, maybe with padded rows; destination: row-major of a
+    # random axis order, maybe padded
+    def row_major(order, pad):
+        st = [0] * rank
+        acc = 1
+        for ax in reversed(order):
+            st[ax] = acc
+            acc *= ext[ax] + (pad if ax == order[-1] else 0)
+        return st
+    ss = row_major(list(range(rank)), int(rng.choice([0, 0, 16] if aligned else [0, 0, 16, 5])))
+    ds = row_major(list(rng.permutation(rank)), int(rng.choice([0, 0, 16])))
+    offs = (int(rng.choice([0, 0, 0, 16] if aligned else [0, 0, 0, 16, 3])),
+            int(rng.choice([0, 0, 0, 32] if aligned else [0, 0, 0, 32, 5])))
+    batch = int(rng.choice([1, 1, 2, 3]))
+    lw = {1: 0, 2: 1, 4: 2, 8: 3, 16: 4}[w]
+
+    def swz():
+        if rng.random() < 0.7:
+            return None
+        bits = int(rng.integers(1, 4))
+        base = int(rng.integers(max(0, 4 - lw), 6)) if aligned else int(rng.integers(0, 4))
+        return (bits, base, int(rng.integers(bits, 6)))
+    return w, ext, ss, ds, offs, batch, swz(), swz()
+
+
+def test_random_permutations_match_oracle():
+    rng = np.random.default_rng(20261202)
+    kernels = collections.Counter()
+    for t in range(80):
+        w, ext, ss, ds, offs, batch, zs, zd = random_case(rng, aligned=t % 2 == 1)
+        p = tpl.tpl_plan(w, ext, ss, ds, offs, batch, src_swizzle=zs, dst_swizzle=zd)
+        assert p.ok, (t, p)
+        kernels[p.kernel] += 1
+        run_case(f"fuzz_{t}", w, ext, ss, ds, offs, batch, seed=t, zs=zs, zd=zd)
+    print("kernel mix:", dict(kernels), flush=True)
+    assert {"lds", "gather", "copy", "quad"} <= set(kernels)
+
+
+def test_graph_capture_and_replay():
+    """The permute captured into a HIP graph (no memset or host sync in the
+    path), replayed three times on new inputs with eager work in between:
+    every replay equals the oracle."""
+    torch = _torch()
+    print("\n[case] graph capture: fp16 128x64 tiles x 512 and SF x 4096", flush=True)
+    t_ext, t_ss, t_ds, t_b = (128, 64), (64, 1), (1, 128), 512
+    f_ext, f_ss, f_ds, f_b = (4, 32), (32, 1), (1, 4), 4096
+    a = torch.empty(t_b * 128 * 64 * 2, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    c = torch.empty(f_b * 128 * 4, dtype=torch.uint8, device="cuda")
+    d = torch.empty_like(c)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        # one eager call first: plans are made outside the capture
+        tpl.permute(b, a, t_ext, t_ss, t_ds, batch=t_b, dtype_bytes=2)
+        tpl.permute(d, c, f_ext, f_ss, f_ds, batch=f_b, dtype_bytes=4)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        tpl.permute(b, a, t_ext, t_ss, t_ds, batch=t_b, dtype_bytes=2)
+        tpl.permute(d, c, f_ext, f_ss, f_ds, batch=f_b, dtype_bytes=4)
+    for rep in range(3):
+        xa = synth.random_bytes(100 + rep, a.numel()).copy()
+        xc = synth.random_bytes(200 + rep, c.numel()).copy()
+        a.copy_(torch.from_numpy(xa))
+        c.copy_(torch.from_numpy(xc))
+        b.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rb = np.empty_like(xa)
+        oracle.permute(xa, rb, 2, t_ext, t_ss, t_ds, (0, 0), t_b)
+        rd = np.empty_like(xc)
+        oracle.permute(xc, rd, 4, f_ext, f_ss, f_ds, (0, 0), f_b)
+        assert np.array_equal(b.cpu().numpy(), rb), rep
+        assert np.array_equal(d.cpu().numpy(), rd), rep
+
+
+def test_two_streams_at_once():
+    torch = _torch()
+    print("\n[case] two streams: bf16 2048^2 transpose and u8 (64,128,32,32) axes (0,2,3,1)", flush=True)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    n = 2048
+    x1 = synth.random_bytes(301, n * n * 2).copy()
+    e2, ss2, ds2 = (64, 128, 32, 32), (131072, 1024, 32, 1), (131072, 1, 4096, 128)
+    x2 = synth.random_bytes(302, 64 * 128 * 32 * 32).copy()
+    a1 = torch.from_numpy(x1).cuda()
+    a2 = torch.from_numpy(x2).cuda()
+    b1, b2 = torch.empty_like(a1), torch.empty_like(a2)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            tpl.permute(b1, a1, (n, n), (n, 1), (1, n), dtype_bytes=2)
+        with torch.cuda.stream(s2):
+            tpl.permute(b2, a2, e2, ss2, ds2, dtype_bytes=1)
+    torch.cuda.synchronize()
+    r1 = np.empty_like(x1)
+    oracle.permute(x1, r1, 2, (n, n), (n, 1), (1, n))
+    r2 = np.empty_like(x2)
+    oracle.permute(x2, r2, 1, e2, ss2, ds2)
+    assert np.array_equal(b1.cpu().numpy(), r1)
+    assert np.array_equal(b2.cpu().numpy(), r2)
