@@ -60,6 +60,22 @@ def traffic_for(name: str):
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
+def lds_counters_for(name: str):
+    """Per-dispatch LDS counters of the dominant kernel (rocprofv3), or None
+    when absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_hash():
+        return None
+    rec = t.get("lds", {}).get(name)
+    if not rec:
+        return None
+    return rec
+
+
 def dtype_name(w: int, specials: bool) -> str:
     return {1: "u8", 2: "u16", 4: "u32", 8: "u64", 16: "u128"}[w]
 
@@ -78,6 +94,8 @@ def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
     import numpy as np
     import oracle
     y = np.empty(wl.elements * wl.w, dtype=np.uint8)
+    oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+                   wl.src_swizzle, wl.dst_swizzle)   # untimed warm-up (first touch of the output)
     runs, t0 = 0, time.perf_counter()
     while True:
         oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
@@ -94,6 +112,59 @@ def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
         "sample": f"the full workload ({wl.elements} elements) permuted {runs} times by the "
                   f"single-threaded C oracle in {el:.1f} s",
     }, y
+
+
+def cpu_baseline_parallel(wl, x, y_ref, min_seconds=5.0, max_runs=200):
+    """The same single-threaded C oracle run on all host cores at once, each
+    thread on a slice of the workload (a range of batch items, or of the first
+    mode when there is one item: the slice's element offsets move by the
+    range start times the item span or the mode's strides, by the buffers
+    page's address rule).  Plain layouts only (a swizzle acts on the
+    unshifted layout offset).  Checked against the single-threaded result."""
+    import concurrent.futures as cf
+    import numpy as np
+    import oracle
+    if wl.src_swizzle or wl.dst_swizzle:
+        return None
+    threads = max(1, min(16, os.cpu_count() or 1))
+    def cos(st):
+        return 1 + sum((e - 1) * s_ for e, s_ in zip(wl.extents, st))
+    if wl.batch > 1:
+        n, unit_s, unit_d = wl.batch, cos(wl.src_strides), cos(wl.dst_strides)
+    else:
+        n, unit_s, unit_d = wl.extents[0], wl.src_strides[0], wl.dst_strides[0]
+    cuts = [n * i // threads for i in range(threads + 1)]
+    parts = [(a, b) for a, b in zip(cuts, cuts[1:]) if b > a]
+    y = np.empty_like(y_ref)
+
+    def one(ab):
+        a, b = ab
+        offs = (wl.offsets[0] + a * unit_s, wl.offsets[1] + a * unit_d)
+        if wl.batch > 1:
+            oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, offs, b - a)
+        else:
+            ext = (b - a,) + tuple(wl.extents[1:])
+            oracle.permute(x, y, wl.w, ext, wl.src_strides, wl.dst_strides, offs, 1)
+
+    with cf.ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        list(ex.map(one, parts))   # untimed: first touch of the output pages
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            list(ex.map(one, parts))
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or runs >= max_runs:
+                break
+    if not np.array_equal(y, y_ref):
+        raise RuntimeError("parallel oracle run disagrees with the single-threaded one")
+    return {
+        "value": round(wl.bytes_moved * runs / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": len(parts),
+        "kind": "oracle-omp",
+        "sample": f"the full workload permuted {runs} times in {el:.1f} s by {len(parts)} host threads, "
+                  f"each running the single-threaded C oracle on a slice",
+    }
 
 
 def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, do_ceiling=True):
@@ -196,6 +267,7 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4),
             "traffic": traffic_for(wl.name),
+            "lds_counters": lds_counters_for(wl.name),
             "kernel_ms_avg": round(avg_ms, 5),
             "host_enqueue_us": round(host_us, 2),
         },
@@ -203,6 +275,7 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
     ref = None
     if do_cpu:
         out["cpu_baseline"], ref = cpu_baseline(wl, x)
+        out["cpu_baseline_parallel"] = cpu_baseline_parallel(wl, x, ref)
     if do_verify:
         import oracle
         if ref is None:
