@@ -39,14 +39,24 @@ def _run(cmd, verbose):
         print("\n".join(msgs))
 
 
+# A plain C++ client of the C ABI used by the tests (host code only, links the library).
+CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_client.cpp")
+CLIENT = os.path.join(ROOT, "tests", "c_abi", "abi_client")
+
+
 def build(verbose: bool = False) -> str:
-    """Build libtpl.so and the LDS bank-geometry probe (both in-tree)."""
+    """Build libtpl.so, the LDS bank-geometry probe and the C ABI test client (all in-tree)."""
     tmp = LIB + ".tmp"
     _run([HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     ptmp = PROBE + ".tmp"
     _run([HIPCC] + PROBE_FLAGS + [os.path.join(CSRC, "lds_probe.hip"), "-o", ptmp], verbose)
     os.replace(ptmp, PROBE)
+    if os.path.exists(CLIENT_SRC):
+        ctmp = CLIENT + ".tmp"
+        _run([HIPCC, "-O2", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"), CLIENT_SRC,
+              "-L", HERE, "-ltpl", "-Wl,-rpath,$ORIGIN/../../tensor_layout_amd", "-o", ctmp], verbose)
+        os.replace(ctmp, CLIENT)
     return LIB
 
 
