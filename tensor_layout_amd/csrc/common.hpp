@@ -190,7 +190,9 @@ struct LdsShape {
     constexpr TPL_HD int read_bytes() const { return w >= 8 ? w : 4; }    // LDS read width
     constexpr TPL_HD int reads_per_group() const { return w >= 8 ? 16 / w : 4 * g(); }  // P of the read phase
     constexpr TPL_HD int nq() const { return tb * w / 16; }              // 16-byte chunks per destination row
-    constexpr TPL_HD int ql() const { return nq() < 8 ? nq() : 8; }      // chunks along b in neighbouring lanes
+    // chunks along b in neighbouring lanes: a wave's store covers 256-byte
+    // runs of destination rows (measured against 128- and 512-byte runs)
+    constexpr TPL_HD int ql() const { return nq() < 16 ? nq() : 16; }
     constexpr TPL_HD int cols() const { return w >= 8 ? ta : ta * w / 4; } // read columns (dwords, or 8-byte elements)
     constexpr TPL_HD int groups() const { return cols() * nq(); }
     constexpr TPL_HD int groups_per_thread() const { return (groups() + threads() - 1) / threads(); }
@@ -210,7 +212,7 @@ TPL_HD int lds_write_addr(const LdsShape& sh, int pitch, int ww, int t, int k, i
 }
 
 // Read phase: thread t, group slot k2, unrolled read step r.
-// Group gid -> (column col, chunk q): lanes run along q first (QL of them),
+// Group gid -> (column col, chunk q): lanes run along q first (ql() of them),
 // then along col, then over the rest of q.
 TPL_HD void lds_group(const LdsShape& sh, int t, int k2, int* col, int* q) {
     int gid = t + k2 * sh.threads();

@@ -229,7 +229,7 @@ def tile_programs(w, tb, ta, cpt, pitch, ww, shift_w, mask_w, shift_r, mask_r):
                     addrs.append((cid // cpr) * pitch + (cid % cpr) * 16 + h * ww)
                 yield True, ww, addrs
     nq = tb * w // 16
-    ql = min(8, nq)
+    ql = min(16, nq)
     cols = ta if w >= 8 else ta * w // 4
     reads = 16 // w if w >= 8 else 4 * (4 // w if w < 4 else 1)
     rb = w if w >= 8 else 4
