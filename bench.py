@@ -311,6 +311,20 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
         ev1.record(stream)
         torch.cuda.synchronize()
         ceiling = 2 * nbytes / (ev0.elapsed_time(ev1) / csteps * 1e-3) / 1e9
+    # Warm: the same launches on one buffer pair, which then stays in the
+    # 256 MB Infinity Cache when it fits (cache-assisted, not the HBM figure).
+    if entry == "permute" and 2 * nbytes <= (200 << 20):
+        p0 = ptrs[0]
+        wsteps = min(steps, 200)
+        for _ in range(10):
+            prepared(*p0, sp)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(wsteps):
+            prepared(*p0, sp)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        out["warm_cache_assisted_gbps"] = round(wl.bytes_moved / (ev0.elapsed_time(ev1) / wsteps * 1e-3) / 1e9, 2)
     out["roofline"]["copy_ceiling_gbps"] = round(ceiling, 2) if ceiling else None
     out["roofline"]["frac_of_copy_ceiling"] = round(achieved / ceiling, 4) if ceiling else None
     del srcs, dsts
