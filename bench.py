@@ -161,7 +161,7 @@ def cpu_baseline_parallel(wl, x, y_ref, min_seconds=5.0, max_runs=200):
         "value": round(wl.bytes_moved * runs / el / 1e9, 4),
         "unit": "GB/s",
         "cores": len(parts),
-        "kind": "oracle-omp",
+        "kind": "oracle-parallel",
         "sample": f"the full workload permuted {runs} times in {el:.1f} s by {len(parts)} host threads, "
                   f"each running the single-threaded C oracle on a slice",
     }
