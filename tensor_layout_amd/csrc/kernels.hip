@@ -153,8 +153,34 @@ __device__ __forceinline__ u32x4 transpose4(u32x4 v, int row, int lane) {
     return y;
 }
 
-template <bool WIDE, int NB, bool BIG, bool SWZ>
+// After transpose4 a lane holds, for rows 0..3, dword j of each row's chunk
+// (d[r] = row r, the 4 / W elements of columns c .. c + 4/W - 1).  Sub-dword
+// elements are then regrouped so that the lane holds those columns one after
+// the other, each as its 4 rows: the 16 destination bytes of 4 / W adjacent
+// columns.
+template <int W>
+__device__ __forceinline__ u32x4 columns_from_rows(u32x4 d) {
+    if constexpr (W == 4) {
+        return d;
+    } else if constexpr (W == 2) {
+        return u32x4{(d.x & 0xffffu) | (d.y << 16), (d.z & 0xffffu) | (d.w << 16),
+                     (d.x >> 16) | (d.y & 0xffff0000u), (d.z >> 16) | (d.w & 0xffff0000u)};
+    } else {
+        u32x4 o;
+        uint32_t* op = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int s = 8 * k;
+            op[k] = ((d.x >> s) & 0xffu) | (((d.y >> s) & 0xffu) << 8) | (((d.z >> s) & 0xffu) << 16) |
+                    (((d.w >> s) & 0xffu) << 24);
+        }
+        return o;
+    }
+}
+
+template <int W, bool WIDE, int NB, bool BIG, bool SWZ>
 __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
+    constexpr int CE = 16 / W;   // elements per 16-byte row chunk
     const int lane = threadIdx.x & 63;
     // WIDE: half-wave h takes unit 2g+h; row r = (lane>>3)&3, column group q = lane&7.
     // narrow: quad qi takes unit 16g+qi; row r = lane&3.
@@ -172,11 +198,12 @@ __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
             split<BIG>(U, a.upr, a.div_upr, item, ua);
             int64_t so, d_o;
             modes_offsets<NB, BIG>(a.batch, item, so, d_o);
-            const int64_t a0 = WIDE ? 32 * ua + 4 * cq : 4 * ua;   // first column this lane loads
-            v = ld16(at<SWZ>(a.src, (so + r * a.s_b + a0) * 4, a.zs));
-            dofs = (d_o + (a0 + r) * a.d_a) * 4;                  // after the exchange: column a0 + r
+            const int64_t a0 = WIDE ? (8 * ua + cq) * CE : ua * CE;   // first column this lane loads
+            v = ld16(at<SWZ>(a.src, (so + r * a.s_b + a0) * W, a.zs));
+            // after the exchange: columns a0 + r * 4/W onwards (adjacent when W < 4)
+            dofs = (d_o + (a0 + r * (4 / W)) * a.d_a) * W;
         }
-        const u32x4 y = transpose4<WIDE>(v, r, lane);
+        const u32x4 y = columns_from_rows<W>(transpose4<WIDE>(v, r, lane));
         if (act) st16(at<SWZ>(a.dst, dofs, a.zd), y);
     }
 }
@@ -583,13 +610,21 @@ static hipError_t launch_nb(const Plan& p, const uint8_t* src, uint8_t* dst, hip
         a.src = src;
         a.dst = dst;
         dim3 grid((unsigned)cap_grid(p.grid, 64)), block(64);
-        if ((a.zs.ymask | a.zd.ymask) == 0) {
-            if (a.wide) hipLaunchKernelGGL((k_quad<true, NB, BIG, false>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_quad<false, NB, BIG, false>), grid, block, 0, st, a);
-        } else {
-            if (a.wide) hipLaunchKernelGGL((k_quad<true, NB, BIG, true>), grid, block, 0, st, a);
-            else hipLaunchKernelGGL((k_quad<false, NB, BIG, true>), grid, block, 0, st, a);
-        }
+        const bool swz = (a.zs.ymask | a.zd.ymask) != 0;
+#define TPL_QUAD_W(W_)                                                                                   \
+    if (p.w == W_) {                                                                                     \
+        if (!swz) {                                                                                      \
+            if (a.wide) hipLaunchKernelGGL((k_quad<W_, true, NB, BIG, false>), grid, block, 0, st, a);   \
+            else hipLaunchKernelGGL((k_quad<W_, false, NB, BIG, false>), grid, block, 0, st, a);         \
+        } else {                                                                                         \
+            if (a.wide) hipLaunchKernelGGL((k_quad<W_, true, NB, BIG, true>), grid, block, 0, st, a);    \
+            else hipLaunchKernelGGL((k_quad<W_, false, NB, BIG, true>), grid, block, 0, st, a);          \
+        }                                                                                                \
+    }
+        TPL_QUAD_W(4)
+        TPL_QUAD_W(2)
+        TPL_QUAD_W(1)
+#undef TPL_QUAD_W
         return hipGetLastError();
     }
     case TPL_KERNEL_LDS: {

@@ -577,14 +577,20 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
         const Mode& mb = sh.m[b];
         bool src_ok = sa % 16 == 0 && all_aligned(sh, a, -1, w, true, 16);
         bool dst_ok = da % 16 == 0 && all_aligned(sh, b, -1, w, false, 16);
-        // 4x4 fp32 blocks transposed inside lane quads.
-        if (vec16 && w == 4 && mb.e == 4 && ma.e % 4 == 0 && src_ok && dst_ok) {
+        // Blocks of 4 rows x one 16-byte chunk transposed inside lane quads:
+        // 4-byte elements with any destination column stride; 1- and 2-byte
+        // elements when the 4/w columns a lane ends up holding are adjacent
+        // in the destination (column stride 4: each column is its 4 rows).
+        const int ce = 16 / w;   // elements per 16-byte chunk
+        const bool quad_w = w == 4 || ((w == 1 || w == 2) && ma.d == 4);
+        const bool dst_ok_q = da % 16 == 0 && all_aligned(sh, b, w < 4 ? a : -1, w, false, 16);
+        if (vec16 && quad_w && mb.e == 4 && ma.e % ce == 0 && src_ok && dst_ok_q) {
             p.kernel = TPL_KERNEL_QUAD;
             QuadArgs& q = p.quad;
-            // Wide units (4 rows x 32 columns, one per 32-lane half-wave) when the
+            // Wide units (4 rows x 8 chunks, one per 32-lane half-wave) when the
             // rows allow it: each row's 128 bytes are then one lane-ordered load.
-            q.wide = (ma.e % 32 == 0) ? 1 : 0;
-            q.upr = q.wide ? ma.e / 32 : ma.e / 4;
+            q.wide = (ma.e * w % 128 == 0) ? 1 : 0;
+            q.upr = q.wide ? ma.e * w / 128 : ma.e / ce;
             q.div_upr = make_fastdiv((uint32_t)std::min<int64_t>(q.upr, 0x7fffffff));
             q.s_b = mb.s;
             q.d_a = ma.d;
@@ -595,7 +601,7 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             set_modes(q.batch, sh, others, no);
             p.P = 4;
             p.tile_b = 4;
-            p.tile_a = q.wide ? 32 : 4;
+            p.tile_a = q.wide ? 128 / w : ce;
             p.block = 64;   // one wave per workgroup
             const int64_t per_wave = q.wide ? 2 : 16;
             p.grid = (q.nunits + per_wave - 1) / per_wave;

@@ -76,6 +76,9 @@ W16_4K = Workload("transpose_4096x4096_16B", 16, (4096, 4096), (4096, 1), (1, 40
 OUTER_PERM = Workload("axes1023_64x128x32x32_f32_runs", 4, (64, 128, 32, 32),
                       (131072, 1024, 32, 1), (1024, 65536, 32, 1), seed=_seed(6))
 
+# The same re-layout for 1-byte (e8m0 / fp8) and 2-byte (fp16) scale factors.
+SF_U8 = Workload("sf_transpose_2^20x4x32_u8", 1, (4, 32), (32, 1), (1, 4), batch=1 << 20, seed=_seed(2, 2))
+SF_F16 = Workload("sf_transpose_2^20x4x32_f16", 2, (4, 32), (32, 1), (1, 4), batch=1 << 20, seed=_seed(2, 3))
 # The SF transpose into XOR-swizzled destination tiles: the 16-byte chunk
 # index of each 128-element tile (bits 2..3 of the offset) is XORed with bits
 # 5..6; the swizzle period is one tile.
@@ -93,7 +96,7 @@ BF16_16K_INPLACE = Workload("transpose_16384x16384_bf16_inplace", 2, (16384, 163
 COPY_CALIBRATION = Workload("identity_copy_512MiB_u32", 4, (1 << 27,), (1,), (1,), seed=0x5EED0100)
 
 ALL = ([SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)]
-       + [BF16_16K, W16_4K, OUTER_PERM, SF_SWIZZLED, TILE_SWIZZLED])
+       + [BF16_16K, W16_4K, OUTER_PERM, SF_SWIZZLED, TILE_SWIZZLED, SF_U8, SF_F16])
 INPLACE = [BF16_16K_INPLACE]
 
 

@@ -151,6 +151,8 @@ EXPECTED_KERNEL = {
     "axes1023_64x128x32x32_f32_runs": "copy",
     "sf_transpose_2^20x4x32_f32_to_swizzled": "quad",
     "tile_65536x128x64_f16_to_swizzled_colmajor": "lds",
+    "sf_transpose_2^20x4x32_u8": "quad",
+    "sf_transpose_2^20x4x32_f16": "quad",
 }
 
 
@@ -516,3 +518,16 @@ def test_swizzled_overlap_uses_the_swizzled_reach():
     assert max(oracle.swizzle(1, 4, 1, m) for m in range(40)) >= 40
     st_ = tpl.tpl_permute_swizzled(sp, sp + 40 * 4, 4, ext, st, st, (0, 0), 1, (1, 4, 1), None)
     assert st_ == tpl.TPL_E_ALIAS, tpl.tpl_last_error()
+
+
+@pytest.mark.parametrize("w,ext,ds,kernel,tile", [
+    (1, (4, 32), (1, 4), "quad", (4, 16)),     # e8m0 / fp8 SF tiles: 16-column units
+    (2, (4, 32), (1, 4), "quad", (4, 8)),
+    (1, (4, 128), (1, 4), "quad", (4, 128)),   # wide: one 4 x 128-byte unit per half-wave
+    (2, (4, 64), (1, 4), "quad", (4, 64)),
+    (1, (4, 32), (1, 8), "gather", (0, 0)),    # columns not adjacent in the destination
+    (2, (4, 12), (1, 4), "gather", (0, 0)),    # rows not a whole number of 16-byte chunks
+])
+def test_sub_dword_quad_selection(w, ext, ds, kernel, tile):
+    p = tpl.tpl_plan(w, ext, (ext[1], 1), ds, batch=64)
+    assert p.ok and p.kernel == kernel and p.tile == tile, p

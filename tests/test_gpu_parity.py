@@ -84,6 +84,8 @@ SMALL = [
     workloads.Workload("transpose_1024x768_bf16", 2, (1024, 768), (768, 1), (1, 1024), seed=0x5EED0050),
     workloads.Workload("transpose_256x192_16B", 16, (256, 192), (192, 1), (1, 256), seed=0x5EED0051),
     workloads.scaled(workloads.SF_SWIZZLED, batch=4097),
+    workloads.scaled(workloads.SF_U8, batch=4099),
+    workloads.scaled(workloads.SF_F16, batch=4101),
     workloads.scaled(workloads.TILE_SWIZZLED, batch=33),
 ]
 
@@ -121,6 +123,11 @@ RAGGED = [
     ("lds_w16_big_tile_ragged", 16, (50, 200), (200, 1), (1, 50), "lds"),
     ("quad_qpr9", 4, (4, 36), (36, 1), (1, 4), "quad"),
     ("quad_padded", 4, (5, 4, 32), (160, 40, 1), (256, 1, 8), "quad"),
+    ("quad_u8_narrow_batched", 1, (7, 4, 48), (256, 64, 1), (208, 1, 4), "quad"),
+    ("quad_u8_wide", 1, (3, 4, 256), (1024, 256, 1), (1024, 1, 4), "quad"),
+    ("quad_u16_narrow_padded_rows", 2, (9, 4, 24), (160, 40, 1), (96, 1, 4), "quad"),
+    ("quad_u16_wide", 2, (5, 4, 128), (512, 128, 1), (512, 1, 4), "quad"),
+    ("gather_u8_columns_apart", 1, (6, 4, 32), (128, 32, 1), (256, 1, 8), "gather"),
     ("copy_outer_perm", 4, (8, 64, 32), (32, 256, 1), (2048, 32, 1), "copy"),
     ("copy_identity", 2, (1000, 64), (64, 1), (64, 1), "copy"),
     ("copy_runs_of_8_bytes", 2, (40, 12), (12, 1), (480, 1), "copy"),
@@ -167,6 +174,23 @@ def test_random_layouts():
 
 # ---------------------------------------------------------------------------
 # in place, overlap, declines, empty
+
+
+@pytest.mark.parametrize("w", [1, 2])
+def test_inplace_sub_dword_sf_transpose(w):
+    """1- and 2-byte SF tiles in place: each batch item is moved inside one
+    wave-instruction by the quad kernel, reads before writes."""
+    torch = _torch()
+    print(f"\n[case] in-place SF transpose, w={w}, 2^16 tiles", flush=True)
+    batch = 1 << 16
+    x = make_input(40 + w, batch * 128 * w)
+    ref = np.empty_like(x)
+    oracle.permute(x, ref, w, (4, 32), (32, 1), (1, 4), (0, 0), batch)
+    assert tpl.tpl_plan(w, (4, 32), (32, 1), (1, 4), batch=batch, geometry=tpl.TPL_GEOM_GFX950_INPLACE).kernel == "quad"
+    buf = torch.from_numpy(x).cuda()
+    tpl.permute(buf, buf, (4, 32), (32, 1), (1, 4), batch=batch, dtype_bytes=w)
+    torch.cuda.synchronize()
+    assert np.array_equal(buf.cpu().numpy(), ref)
 
 
 def test_inplace_sf_transpose():
