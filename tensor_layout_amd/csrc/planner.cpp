@@ -584,7 +584,13 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
         const int ce = 16 / w;   // elements per 16-byte chunk
         const bool quad_w = w == 4 || ((w == 1 || w == 2) && ma.d == 4);
         const bool dst_ok_q = da % 16 == 0 && all_aligned(sh, b, w < 4 ? a : -1, w, false, 16);
-        if (vec16 && quad_w && mb.e == 4 && ma.e % ce == 0 && src_ok && dst_ok_q) {
+        // 4-byte elements with a longer destination-contiguous mode (e.g. an
+        // array of 4- or 8-float records to one array per field) when the LDS
+        // tile does not apply: blocks of 4 rows along it become one more batch
+        // mode, the fastest, so a wave reads consecutive records.
+        const bool lds_fits = ma.e * w >= 64 && mb.e * w >= 64;
+        const bool quad_rows = mb.e == 4 || (w == 4 && mb.e % 4 == 0 && !lds_fits && sh.rank < kMaxShard);
+        if (vec16 && quad_w && quad_rows && ma.e % ce == 0 && src_ok && dst_ok_q) {
             p.kernel = TPL_KERNEL_QUAD;
             QuadArgs& q = p.quad;
             // Wide units (4 rows x 8 chunks, one per 32-lane half-wave) when the
@@ -594,11 +600,20 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             q.div_upr = make_fastdiv((uint32_t)std::min<int64_t>(q.upr, 0x7fffffff));
             q.s_b = mb.s;
             q.d_a = ma.d;
+            Shard qs = sh;
+            int qidx[kMaxShard + 1];
+            int nq = 0;
+            for (int i = 0; i < no; ++i) qidx[nq++] = others[i];
+            if (mb.e > 4) {
+                qs.m[qs.rank] = Mode{mb.e / 4, 4 * mb.s, 4 * mb.d};
+                qidx[nq++] = qs.rank++;
+            }
             int64_t items = 1;
-            for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
+            for (int i = 0; i < nq; ++i) items *= qs.m[qidx[i]].e;
             q.nunits = items * q.upr;
             if (q.nunits >= ((int64_t)1 << 31)) p.big = true;
-            set_modes(q.batch, sh, others, no);
+            set_modes(q.batch, qs, qidx, nq);
+            p.batch_modes = nq;
             p.P = 4;
             p.tile_b = 4;
             p.tile_a = q.wide ? 128 / w : ce;
@@ -607,7 +622,7 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             p.grid = (q.nunits + per_wave - 1) / per_wave;
             // One wave-instruction moves each batch item (all its loads complete
             // before its stores) when the item's units tile the wave evenly.
-            p.unit_is_item = q.wide ? (q.upr <= 2) : (q.upr <= 16 && 16 % q.upr == 0);
+            p.unit_is_item = mb.e == 4 && (q.wide ? (q.upr <= 2) : (q.upr <= 16 && 16 % q.upr == 0));
             return p;
         }
         // Tiled LDS transpose.

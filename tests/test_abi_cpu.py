@@ -153,6 +153,7 @@ EXPECTED_KERNEL = {
     "tile_65536x128x64_f16_to_swizzled_colmajor": "lds",
     "sf_transpose_2^20x4x32_u8": "quad",
     "sf_transpose_2^20x4x32_f16": "quad",
+    "aos_to_soa_2^24x4_f32": "quad",
 }
 
 
@@ -531,3 +532,17 @@ def test_swizzled_overlap_uses_the_swizzled_reach():
 def test_sub_dword_quad_selection(w, ext, ds, kernel, tile):
     p = tpl.tpl_plan(w, ext, (ext[1], 1), ds, batch=64)
     assert p.ok and p.kernel == kernel and p.tile == tile, p
+
+
+@pytest.mark.parametrize("ext,kernel", [
+    ((1000, 4), "quad"), ((1000, 8), "quad"), ((1000, 12), "quad"),   # records of 4, 8, 12 floats
+    ((1000, 16), "lds"),                                             # 64-byte records: the LDS tile
+    ((1002, 4), "gather"),                                           # not whole blocks of 4 records
+])
+def test_aos_to_soa_selection(ext, kernel):
+    n, c = ext
+    p = tpl.tpl_plan(4, ext, (c, 1), (1, n), batch=1)
+    assert p.ok and p.kernel == kernel, p
+    # in place it is not a per-unit move: refused
+    q = tpl.tpl_plan(4, ext, (c, 1), (1, n), geometry=tpl.TPL_GEOM_GFX950_INPLACE)
+    assert q.status == tpl.TPL_E_ALIAS

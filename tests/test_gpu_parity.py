@@ -128,6 +128,9 @@ RAGGED = [
     ("quad_u16_narrow_padded_rows", 2, (9, 4, 24), (160, 40, 1), (96, 1, 4), "quad"),
     ("quad_u16_wide", 2, (5, 4, 128), (512, 128, 1), (512, 1, 4), "quad"),
     ("gather_u8_columns_apart", 1, (6, 4, 32), (128, 32, 1), (256, 1, 8), "gather"),
+    ("quad_aos_to_soa_f32x4", 4, (100000, 4), (4, 1), (1, 100000), "quad"),
+    ("quad_aos_to_soa_f32x8_batched", 4, (3, 4096, 8), (32768, 8, 1), (32768, 1, 4096), "quad"),
+    ("quad_aos_to_soa_f32x12_padded", 4, (2000, 12), (16, 1), (1, 2048), "quad"),
     ("copy_outer_perm", 4, (8, 64, 32), (32, 256, 1), (2048, 32, 1), "copy"),
     ("copy_identity", 2, (1000, 64), (64, 1), (64, 1), "copy"),
     ("copy_runs_of_8_bytes", 2, (40, 12), (12, 1), (480, 1), "copy"),
