@@ -584,12 +584,11 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
         const int ce = 16 / w;   // elements per 16-byte chunk
         const bool quad_w = w == 4 || ((w == 1 || w == 2) && ma.d == 4);
         const bool dst_ok_q = da % 16 == 0 && all_aligned(sh, b, w < 4 ? a : -1, w, false, 16);
-        // 4-byte elements with a longer destination-contiguous mode (e.g. an
-        // array of 4- or 8-float records to one array per field) when the LDS
-        // tile does not apply: blocks of 4 rows along it become one more batch
-        // mode, the fastest, so a wave reads consecutive records.
+        // 4-byte elements with a longer destination-contiguous mode (records
+        // of 4..12 floats to field arrays, or back) when the LDS tile does not
+        // apply: blocks of 4 rows along it become one more batch mode.
         const bool lds_fits = ma.e * w >= 64 && mb.e * w >= 64;
-        const bool quad_rows = mb.e == 4 || (w == 4 && mb.e % 4 == 0 && !lds_fits && sh.rank < kMaxShard);
+        const bool quad_rows = mb.e == 4 || (w == 4 && mb.e % 4 == 0 && !lds_fits && sh.rank + 2 <= kMaxShard);
         if (vec16 && quad_w && quad_rows && ma.e % ce == 0 && src_ok && dst_ok_q) {
             p.kernel = TPL_KERNEL_QUAD;
             QuadArgs& q = p.quad;
@@ -601,10 +600,23 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             q.s_b = mb.s;
             q.d_a = ma.d;
             Shard qs = sh;
-            int qidx[kMaxShard + 1];
+            int qidx[kMaxShard + 2];
             int nq = 0;
             for (int i = 0; i < no; ++i) qidx[nq++] = others[i];
-            if (mb.e > 4) {
+            if (mb.e > 4 && mb.e / 4 < ma.e / ce) {
+                // Few row blocks, many chunks (a field array to records of 8
+                // or 12 floats): chunks and then row blocks, fastest, as batch
+                // modes of narrow units, so a wave writes whole records.
+                q.wide = 0;
+                q.upr = 1;
+                q.div_upr = make_fastdiv(1);
+                qs.m[qs.rank] = Mode{ma.e / ce, ce * ma.s, ce * ma.d};
+                qidx[nq++] = qs.rank++;
+                qs.m[qs.rank] = Mode{mb.e / 4, 4 * mb.s, 4 * mb.d};
+                qidx[nq++] = qs.rank++;
+            } else if (mb.e > 4) {
+                // Many row blocks (records to field arrays): the blocks as the
+                // fastest batch mode, the few chunks of a record inside a unit.
                 qs.m[qs.rank] = Mode{mb.e / 4, 4 * mb.s, 4 * mb.d};
                 qidx[nq++] = qs.rank++;
             }

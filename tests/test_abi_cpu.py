@@ -546,3 +546,13 @@ def test_aos_to_soa_selection(ext, kernel):
     # in place it is not a per-unit move: refused
     q = tpl.tpl_plan(4, ext, (c, 1), (1, n), geometry=tpl.TPL_GEOM_GFX950_INPLACE)
     assert q.status == tpl.TPL_E_ALIAS
+
+
+@pytest.mark.parametrize("c", [8, 12])
+def test_soa_to_aos_selection(c):
+    """Field arrays to records of 8 or 12 floats: narrow quad units walking the
+    row blocks fastest (one chunk mode and one block mode among the batch)."""
+    n = 4096
+    p = tpl.tpl_plan(4, (c, n), (n, 1), (1, c))
+    assert p.ok and p.kernel == "quad" and p.tile == (4, 4), p
+    assert p.grid == (n // 4) * (c // 4) // 16

@@ -131,6 +131,8 @@ RAGGED = [
     ("quad_aos_to_soa_f32x4", 4, (100000, 4), (4, 1), (1, 100000), "quad"),
     ("quad_aos_to_soa_f32x8_batched", 4, (3, 4096, 8), (32768, 8, 1), (32768, 1, 4096), "quad"),
     ("quad_aos_to_soa_f32x12_padded", 4, (2000, 12), (16, 1), (1, 2048), "quad"),
+    ("quad_soa_to_aos_f32x8", 4, (8, 100000), (100000, 1), (1, 8), "quad"),
+    ("quad_soa_to_aos_f32x12_batched", 4, (2, 12, 4096), (12 * 4096, 4096, 1), (12 * 4096, 1, 12), "quad"),
     ("copy_outer_perm", 4, (8, 64, 32), (32, 256, 1), (2048, 32, 1), "copy"),
     ("copy_identity", 2, (1000, 64), (64, 1), (64, 1), "copy"),
     ("copy_runs_of_8_bytes", 2, (40, 12), (12, 1), (480, 1), "copy"),
