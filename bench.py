@@ -80,10 +80,26 @@ def dtype_name(w: int, specials: bool) -> str:
     return {1: "u8", 2: "u16", 4: "u32", 8: "u64", 16: "u128"}[w]
 
 
+def buffer_bytes(wl):
+    """(source, destination) buffer sizes in bytes: each side's element offset
+    plus its batch of item spans (the cosize), widened to the reach of its
+    swizzle.  Every byte a launch touches lies below these sizes."""
+    from tensor_layout_amd import tpl
+
+    def side(off, strides, z):
+        if wl.elements == 0:
+            return 0
+        span = 1 + sum((e - 1) * st for e, st in zip(wl.extents, strides))
+        return (off + tpl._swz_reach(wl.batch * span, z)) * wl.w
+
+    return (side(wl.offsets[0], wl.src_strides, wl.src_swizzle),
+            side(wl.offsets[1], wl.dst_strides, wl.dst_swizzle))
+
+
 def make_input(wl):
     import numpy as np
     from tensor_layout_amd import synth
-    x = synth.random_bytes(wl.seed, wl.elements * wl.w).copy()
+    x = synth.random_bytes(wl.seed, buffer_bytes(wl)[0]).copy()
     if wl.specials and wl.w == 4:
         synth.inject_f32_specials(x.view(np.uint32), wl.seed ^ 0x5EC1A1)
     return x
@@ -93,7 +109,7 @@ def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
     """The oracle as it stands, single-threaded, on the full workload."""
     import numpy as np
     import oracle
-    y = np.empty(wl.elements * wl.w, dtype=np.uint8)
+    y = np.zeros(buffer_bytes(wl)[1], dtype=np.uint8)
     oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
                    wl.src_swizzle, wl.dst_swizzle)   # untimed warm-up (first touch of the output)
     runs, t0 = 0, time.perf_counter()
@@ -174,14 +190,19 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
 
     dev = torch.device("cuda:0")
     x = make_input(wl)
-    nbytes = wl.elements * wl.w
-    pairs = max(2, min(128, math.ceil(ROTATE_BYTES / (2 * nbytes))))
+    ns, nd = buffer_bytes(wl)
+    if wl.inplace:
+        # one buffer holds both layouts' footprints
+        ns = nd = max(ns, nd)
+        x = np.concatenate([x, np.zeros(ns - x.size, dtype=np.uint8)])
+    nbytes = wl.elements * wl.w     # the bytes a launch moves each way
+    pairs = max(2, min(128, math.ceil(ROTATE_BYTES / (ns + nd))))
     srcs = [torch.from_numpy(x).to(dev)]
     for _ in range(pairs - 1):
         srcs.append(srcs[0].clone())
     # In place: each step transposes its buffer again, so a buffer alternates
     # between the input and its transpose.
-    dsts = srcs if wl.inplace else [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(pairs)]
+    dsts = srcs if wl.inplace else [torch.zeros(nd, dtype=torch.uint8, device=dev) for _ in range(pairs)]
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     plan = tpl.tpl_plan(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
@@ -279,7 +300,7 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
     if do_verify:
         import oracle
         if ref is None:
-            ref = np.empty(nbytes, dtype=np.uint8)
+            ref = x.copy() if wl.inplace else np.zeros(nd, dtype=np.uint8)
             oracle.permute(x, ref, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
                            wl.src_swizzle, wl.dst_swizzle)
         if wl.inplace:
@@ -297,7 +318,8 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
     # the same bytes (the library's identity-layout copy, 16-byte vectors)
     # over the same buffer rotation, timed the same way.
     ceiling = None
-    if do_ceiling and nbytes % 16 == 0 and entry == "permute":
+    # (the copy moves the launch's byte count, within both buffers)
+    if do_ceiling and nbytes % 16 == 0 and nbytes <= min(ns, nd) and entry == "permute":
         ident = tpl.PreparedPermute(16, (nbytes // 16,), (1,), (1,))
         cptrs = [(srcs[i].data_ptr(), (srcs[(i + 1) % pairs] if wl.inplace else dsts[i]).data_ptr())
                  for i in range(pairs)]

@@ -138,7 +138,8 @@ struct QuadArgs {
     int64_t upr;
     int64_t s_b;         // source stride of the 4-row mode (elements)
     int64_t d_a;         // destination stride of the contiguous-source mode (elements)
-    int32_t wide;        // 1: 4x32 blocks, lane-ordered 128-byte row loads
+    int32_t wide;        // 1: 4 rows x 8 chunks per half-wave, lane-ordered 128-byte row loads
+    int32_t split;       // 1: sub-dword columns stored one by one (not adjacent in the destination)
     Modes batch;
     Swz zs, zd;          // operand swizzles (byte form)
 };

@@ -178,8 +178,11 @@ __device__ __forceinline__ u32x4 columns_from_rows(u32x4 d) {
     }
 }
 
-template <int W, bool WIDE, int NB, bool BIG, bool SWZ>
+// SPLIT (W < 4 only): the lane's 4/W columns are not adjacent in the
+// destination; each column's 4 rows (4 W bytes) are stored on their own.
+template <int W, bool WIDE, int NB, bool BIG, bool SWZ, bool SPLIT>
 __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
+    static_assert(!SPLIT || W < 4, "split stores are for sub-dword elements");
     constexpr int CE = 16 / W;   // elements per 16-byte row chunk
     const int lane = threadIdx.x & 63;
     // WIDE: half-wave h takes unit 2g+h; row r = (lane>>3)&3, column group q = lane&7.
@@ -200,11 +203,23 @@ __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
             modes_offsets<NB, BIG>(a.batch, item, so, d_o);
             const int64_t a0 = WIDE ? (8 * ua + cq) * CE : ua * CE;   // first column this lane loads
             v = ld16(at<SWZ>(a.src, (so + r * a.s_b + a0) * W, a.zs));
-            // after the exchange: columns a0 + r * 4/W onwards (adjacent when W < 4)
+            // after the exchange: columns a0 + r * 4/W onwards (adjacent unless SPLIT)
             dofs = (d_o + (a0 + r * (4 / W)) * a.d_a) * W;
         }
         const u32x4 y = columns_from_rows<W>(transpose4<WIDE>(v, r, lane));
-        if (act) st16(at<SWZ>(a.dst, dofs, a.zd), y);
+        if (act) {
+            if constexpr (!SPLIT) {
+                st16(at<SWZ>(a.dst, dofs, a.zd), y);
+            } else if constexpr (W == 2) {
+                __builtin_nontemporal_store(u32x2{y.x, y.y}, reinterpret_cast<u32x2*>(at<SWZ>(a.dst, dofs, a.zd)));
+                __builtin_nontemporal_store(u32x2{y.z, y.w},
+                                            reinterpret_cast<u32x2*>(at<SWZ>(a.dst, dofs + a.d_a * 2, a.zd)));
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    __builtin_nontemporal_store(y[k], reinterpret_cast<uint32_t*>(at<SWZ>(a.dst, dofs + k * a.d_a, a.zd)));
+            }
+        }
     }
 }
 
@@ -611,19 +626,21 @@ static hipError_t launch_nb(const Plan& p, const uint8_t* src, uint8_t* dst, hip
         a.dst = dst;
         dim3 grid((unsigned)cap_grid(p.grid, 64)), block(64);
         const bool swz = (a.zs.ymask | a.zd.ymask) != 0;
-#define TPL_QUAD_W(W_)                                                                                   \
-    if (p.w == W_) {                                                                                     \
-        if (!swz) {                                                                                      \
-            if (a.wide) hipLaunchKernelGGL((k_quad<W_, true, NB, BIG, false>), grid, block, 0, st, a);   \
-            else hipLaunchKernelGGL((k_quad<W_, false, NB, BIG, false>), grid, block, 0, st, a);         \
-        } else {                                                                                         \
-            if (a.wide) hipLaunchKernelGGL((k_quad<W_, true, NB, BIG, true>), grid, block, 0, st, a);    \
-            else hipLaunchKernelGGL((k_quad<W_, false, NB, BIG, true>), grid, block, 0, st, a);          \
-        }                                                                                                \
+#define TPL_QUAD_W(W_, SP_)                                                                                   \
+    if (p.w == W_ && a.split == (SP_ ? 1 : 0)) {                                                             \
+        if (!swz) {                                                                                          \
+            if (a.wide) hipLaunchKernelGGL((k_quad<W_, true, NB, BIG, false, SP_>), grid, block, 0, st, a);   \
+            else hipLaunchKernelGGL((k_quad<W_, false, NB, BIG, false, SP_>), grid, block, 0, st, a);         \
+        } else {                                                                                             \
+            if (a.wide) hipLaunchKernelGGL((k_quad<W_, true, NB, BIG, true, SP_>), grid, block, 0, st, a);    \
+            else hipLaunchKernelGGL((k_quad<W_, false, NB, BIG, true, SP_>), grid, block, 0, st, a);          \
+        }                                                                                                    \
     }
-        TPL_QUAD_W(4)
-        TPL_QUAD_W(2)
-        TPL_QUAD_W(1)
+        TPL_QUAD_W(4, false)
+        TPL_QUAD_W(2, false)
+        TPL_QUAD_W(1, false)
+        TPL_QUAD_W(2, true)
+        TPL_QUAD_W(1, true)
 #undef TPL_QUAD_W
         return hipGetLastError();
     }

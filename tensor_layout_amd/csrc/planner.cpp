@@ -577,21 +577,31 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
         const Mode& mb = sh.m[b];
         bool src_ok = sa % 16 == 0 && all_aligned(sh, a, -1, w, true, 16);
         bool dst_ok = da % 16 == 0 && all_aligned(sh, b, -1, w, false, 16);
-        // Blocks of 4 rows x one 16-byte chunk transposed inside lane quads:
-        // 4-byte elements with any destination column stride; 1- and 2-byte
-        // elements when the 4/w columns a lane ends up holding are adjacent
-        // in the destination (column stride 4: each column is its 4 rows).
+        // Blocks of 4 rows x one 16-byte chunk transposed inside lane quads.
+        // A lane ends up with 16 destination bytes: one column of 4-byte
+        // elements, or 4/w columns of 1- or 2-byte elements, stored as one
+        // piece when adjacent in the destination (column stride 4) and one
+        // column at a time otherwise.
         const int ce = 16 / w;   // elements per 16-byte chunk
-        const bool quad_w = w == 4 || ((w == 1 || w == 2) && ma.d == 4);
-        const bool dst_ok_q = da % 16 == 0 && all_aligned(sh, b, w < 4 ? a : -1, w, false, 16);
-        // 4-byte elements with a longer destination-contiguous mode (records
-        // of 4..12 floats to field arrays, or back) when the LDS tile does not
-        // apply: blocks of 4 rows along it become one more batch mode.
+        // Sub-dword columns that are not adjacent in the destination are
+        // stored one by one, 4 w bytes each (every destination offset a
+        // multiple of 4 elements), but only where neighbouring lanes' pieces
+        // fill whole lines: along a destination-contiguous mode longer than
+        // the 4-row block.  Isolated pieces (a tile of 4 rows with gaps
+        // between its columns) measured slower than the element-wise kernel.
+        const bool split = w < 4 && ma.d != 4;
+        const bool quad_w = w == 4 || (w < 4 && (!split || mb.e > 4));
+        const bool dst_ok_q = split ? (da % (4 * w) == 0 && all_aligned(sh, b, -1, w, false, 4 * w))
+                                    : (da % 16 == 0 && all_aligned(sh, b, w < 4 ? a : -1, w, false, 16));
+        // A longer destination-contiguous mode (records of 16-48 bytes to
+        // field arrays, or back) when the LDS tile does not apply: blocks of
+        // 4 rows along it become one more batch mode.
         const bool lds_fits = ma.e * w >= 64 && mb.e * w >= 64;
-        const bool quad_rows = mb.e == 4 || (w == 4 && mb.e % 4 == 0 && !lds_fits && sh.rank + 2 <= kMaxShard);
+        const bool quad_rows = mb.e == 4 || (mb.e % 4 == 0 && !lds_fits && sh.rank + 2 <= kMaxShard);
         if (vec16 && quad_w && quad_rows && ma.e % ce == 0 && src_ok && dst_ok_q) {
             p.kernel = TPL_KERNEL_QUAD;
             QuadArgs& q = p.quad;
+            q.split = split ? 1 : 0;
             // Wide units (4 rows x 8 chunks, one per 32-lane half-wave) when the
             // rows allow it: each row's 128 bytes are then one lane-ordered load.
             q.wide = (ma.e * w % 128 == 0) ? 1 : 0;

@@ -526,7 +526,7 @@ def test_swizzled_overlap_uses_the_swizzled_reach():
     (2, (4, 32), (1, 4), "quad", (4, 8)),
     (1, (4, 128), (1, 4), "quad", (4, 128)),   # wide: one 4 x 128-byte unit per half-wave
     (2, (4, 64), (1, 4), "quad", (4, 64)),
-    (1, (4, 32), (1, 8), "gather", (0, 0)),    # columns not adjacent in the destination
+    (1, (4, 32), (1, 8), "gather", (0, 0)),    # a 4-row tile with gaps between its columns
     (2, (4, 12), (1, 4), "gather", (0, 0)),    # rows not a whole number of 16-byte chunks
 ])
 def test_sub_dword_quad_selection(w, ext, ds, kernel, tile):
@@ -556,3 +556,38 @@ def test_soa_to_aos_selection(c):
     p = tpl.tpl_plan(4, (c, n), (n, 1), (1, c))
     assert p.ok and p.kernel == "quad" and p.tile == (4, 4), p
     assert p.grid == (n // 4) * (c // 4) // 16
+
+
+@pytest.mark.parametrize("w,ext,ss,ds", [
+    (2, (4096, 8), (8, 1), (1, 4096)),     # fp16 x 8 records to field arrays
+    (1, (4096, 16), (16, 1), (1, 4096)),   # u8 x 16 records to field arrays
+    (2, (8, 4096), (4096, 1), (1, 8)),     # and back
+])
+def test_sub_dword_record_layouts_use_the_quad_kernel(w, ext, ss, ds):
+    p = tpl.tpl_plan(w, ext, ss, ds)
+    assert p.ok and p.kernel == "quad", p
+
+
+def test_bench_buffers_cover_every_layout():
+    """bench.py sizes its buffers from the layouts (cosize, offsets, swizzle
+    reach), not from the element count: the oracle's range check passes on
+    buffers of exactly those sizes, for the workloads and for layouts whose
+    destination has gaps."""
+    import numpy as np
+    import bench
+    import oracle
+    W = workloads.Workload
+    cases = [workloads.scaled(wl, batch=min(wl.batch, 64)) if wl.batch > 1 else wl
+             for wl in workloads.ALL if wl.elements * wl.w <= (64 << 20) or wl.batch > 1]
+    cases += [W("sf_u8_column_stride_8", 1, (4, 32), (32, 1), (1, 8), batch=1000),
+              W("padded_rows_offsets", 2, (100, 60), (64, 1), (1, 112), offsets=(5, 9), batch=3),
+              W("swizzled_gap", 4, (40,), (1,), (1,), batch=3, src_swizzle=(1, 4, 1))]
+    for wl in cases:
+        ns, nd = bench.buffer_bytes(wl)
+        x = np.zeros(ns, dtype=np.uint8)
+        y = np.zeros(nd, dtype=np.uint8)
+        oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+                       wl.src_swizzle, wl.dst_swizzle)
+    # the undersized dense guess would not hold the gapped destination
+    wl = cases[-3]
+    assert bench.buffer_bytes(wl)[1] > wl.elements * wl.w

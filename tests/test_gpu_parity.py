@@ -128,6 +128,11 @@ RAGGED = [
     ("quad_u16_narrow_padded_rows", 2, (9, 4, 24), (160, 40, 1), (96, 1, 4), "quad"),
     ("quad_u16_wide", 2, (5, 4, 128), (512, 128, 1), (512, 1, 4), "quad"),
     ("gather_u8_columns_apart", 1, (6, 4, 32), (128, 32, 1), (256, 1, 8), "gather"),
+    ("quad_soa_to_aos_u8x16_split", 1, (16, 4096), (4096, 1), (1, 16), "quad"),
+    ("quad_aos_to_soa_u16x8_split_padded", 2, (2048, 8), (8, 1), (1, 2056), "quad"),
+    ("quad_aos_to_soa_f16x8", 2, (40000, 8), (8, 1), (1, 40000), "quad"),
+    ("quad_aos_to_soa_u8x16_batched", 1, (2, 8192, 16), (8192 * 16, 16, 1), (8192 * 16, 1, 8192), "quad"),
+    ("quad_soa_to_aos_f16x8", 2, (8, 40000), (40000, 1), (1, 8), "quad"),
     ("quad_aos_to_soa_f32x4", 4, (100000, 4), (4, 1), (1, 100000), "quad"),
     ("quad_aos_to_soa_f32x8_batched", 4, (3, 4096, 8), (32768, 8, 1), (32768, 1, 4096), "quad"),
     ("quad_aos_to_soa_f32x12_padded", 4, (2000, 12), (16, 1), (1, 2048), "quad"),

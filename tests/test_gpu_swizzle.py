@@ -26,6 +26,7 @@ CASES = [
     ("sf_8B_granules_elementwise", 4, (4, 32), (32, 1), (1, 4), 513, None, (3, 1, 3), "gather"),
     ("sf_u8_dst_swizzled", 1, (4, 32), (32, 1), (1, 4), 1025, None, (2, 4, 3), "quad"),
     ("sf_u16_src_swizzled", 2, (4, 32), (32, 1), (1, 4), 1027, (2, 3, 3), None, "quad"),
+    ("aos_to_soa_f16x8_split_dst_swizzled", 2, (4096, 8), (8, 1), (1, 4096), 3, None, (2, 3, 4), "quad"),
     ("f16_tiles_mma_colmajor", 2, (128, 64), (64, 1), (1, 128), 17, None, (3, 3, 4), "lds"),
     ("u8_256_both", 1, (256, 256), (256, 1), (1, 256), 2, (3, 4, 4), (3, 4, 5), "lds"),
     ("u64_src", 8, (64, 64), (64, 1), (1, 64), 3, (2, 1, 3), None, "lds"),
