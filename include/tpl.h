@@ -67,7 +67,9 @@ enum {
     TPL_KERNEL_LDS = 3,    /* tiled 2-D transpose staged through LDS with XOR-ordered phases */
     TPL_KERNEL_REG16 = 4,  /* 16-byte elements: 8x8 element blocks, pure lane remap */
     TPL_KERNEL_COPY = 5,   /* both sides contiguous along one mode: vector copy of runs */
-    TPL_KERNEL_SWAP = 6    /* in-place square transpose: mirrored tile pairs swapped through LDS */
+    TPL_KERNEL_SWAP = 6,   /* in-place square transpose: mirrored tile pairs swapped through LDS */
+    TPL_KERNEL_REC = 7     /* records of any size to field rows or back: the dense side as one
+                              contiguous block through LDS */
 };
 
 /*

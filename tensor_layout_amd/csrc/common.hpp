@@ -163,6 +163,22 @@ struct LdsArgs {
     Swz zs, zd;          // operand swizzles (byte form)
 };
 
+// Records kernel: a tile of TR consecutive records of F fields each, the
+// dense side (whole records one after the other) moved as one contiguous
+// block, the other side one row per field.
+struct RecArgs {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t nrec;        // records per batch item
+    int64_t ntr;         // tiles per batch item
+    FastDiv div_ntr;
+    int64_t ntiles;      // tiles overall
+    int64_t fstride;     // field stride on the sparse side (elements)
+    int32_t F;           // fields per record
+    int32_t TR;          // records per full tile (a multiple of 16 / w)
+    Modes batch;
+};
+
 struct Reg16Args {
     const uint8_t* src;
     uint8_t* dst;

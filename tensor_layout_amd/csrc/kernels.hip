@@ -523,6 +523,82 @@ __global__ void __launch_bounds__(T * T * W / (16 * CPT)) k_swap(LdsArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Records kernel (layouts whose short side is a whole record of F fields,
+// any F: float3 or RGB records to field arrays and back).  The tile holds
+// TR consecutive records in LDS in record order, element (r, f) at byte
+// (r F + f) W.  DENSE_SRC: the source tile is one contiguous block (records
+// one after the other), loaded as 16-byte chunks; every field's TR elements
+// then leave as 16-byte pieces of that field's destination row.  Otherwise
+// the mirror: 16-byte pieces of each field's source row in, the contiguous
+// destination block out.  A tile with fewer than TR records goes element
+// by element through the same LDS layout.
+
+template <int W, bool DENSE_SRC, int NB, bool BIG>
+__global__ void __launch_bounds__(256) k_rec(RecArgs a) {
+    constexpr int NT = 256;
+    constexpr int CE = 16 / W;   // elements per 16-byte piece
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int t = threadIdx.x;
+    const int F = a.F;
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        int64_t item, ti;
+        split<BIG>(tile, a.ntr, a.div_ntr, item, ti);
+        int64_t so, d_o;
+        modes_offsets<NB, BIG>(a.batch, item, so, d_o);
+        const int64_t r0 = ti * a.TR;
+        const int nr = (int)(a.nrec - r0 < a.TR ? a.nrec - r0 : a.TR);
+        const int nel = nr * F;
+        // element (r, f) of this tile: dense side at block + r F + f, sparse
+        // side at row f: f * fstride + r0 + r
+        const int64_t block = DENSE_SRC ? so + r0 * F : d_o + r0 * F;
+        const int64_t rows = DENSE_SRC ? d_o + r0 : so + r0;
+        if (nr == a.TR) {
+            const int nchunks = nel * W / 16;    // == F * TR / CE
+            const int nq = a.TR / CE;            // pieces per field row
+            if constexpr (DENSE_SRC) {
+                for (int c = t; c < nchunks; c += NT)
+                    *reinterpret_cast<u32x4*>(lds + c * 16) = ld16(a.src + block * W + (int64_t)c * 16);
+            } else {
+                for (int g = t; g < nchunks; g += NT) {
+                    const int q = g % nq, f = g / nq;
+                    const u32x4 v = ld16(a.src + (rows + f * a.fstride + (int64_t)q * CE) * W);
+                    const uint8_t* vb = reinterpret_cast<const uint8_t*>(&v);
+#pragma unroll
+                    for (int k = 0; k < CE; ++k) copy_elem<W>(lds + ((q * CE + k) * F + f) * W, vb + k * W);
+                }
+            }
+            __syncthreads();
+            if constexpr (DENSE_SRC) {
+                for (int g = t; g < nchunks; g += NT) {
+                    const int q = g % nq, f = g / nq;
+                    u32x4 v;
+                    uint8_t* vb = reinterpret_cast<uint8_t*>(&v);
+#pragma unroll
+                    for (int k = 0; k < CE; ++k) copy_elem<W>(vb + k * W, lds + ((q * CE + k) * F + f) * W);
+                    st16(a.dst + (rows + f * a.fstride + (int64_t)q * CE) * W, v);
+                }
+            } else {
+                for (int c = t; c < nchunks; c += NT)
+                    st16(a.dst + block * W + (int64_t)c * 16, *reinterpret_cast<const u32x4*>(lds + c * 16));
+            }
+        } else {
+            for (int i = t; i < nel; i += NT) {
+                const int f = i / nr, r = i % nr;
+                const uint8_t* sp = DENSE_SRC ? a.src + (block + r * F + f) * W : a.src + (rows + f * a.fstride + r) * W;
+                copy_elem<W>(lds + (r * F + f) * W, sp);
+            }
+            __syncthreads();
+            for (int i = t; i < nel; i += NT) {
+                const int f = i / nr, r = i % nr;
+                uint8_t* dp = DENSE_SRC ? a.dst + (rows + f * a.fstride + r) * W : a.dst + (block + r * F + f) * W;
+                copy_elem<W>(dp, lds + (r * F + f) * W);
+            }
+        }
+        __syncthreads();   // LDS is reused by the next tile of this workgroup
+    }
+}
+
+// ---------------------------------------------------------------------------
 // 16-byte elements: a wave takes an 8x8 element block; lane (i, j) loads
 // source row b0+i, element a0+j (eight lanes per 128-byte source line) and
 // stores it at destination row a0+j, element b0+i (eight lanes per 128-byte
@@ -656,6 +732,24 @@ static hipError_t launch_nb(const Plan& p, const uint8_t* src, uint8_t* dst, hip
         a.dst = dst;
         return launch_swap<NB, BIG>(p, a, st);
     }
+    case TPL_KERNEL_REC: {
+        RecArgs a = p.rec;
+        a.src = src;
+        a.dst = dst;
+        dim3 grid((unsigned)cap_grid(p.grid, 256)), block(256);
+#define TPL_REC_W(W_)                                                                                   \
+    if (p.w == W_) {                                                                                    \
+        if (p.rec_dense_src) hipLaunchKernelGGL((k_rec<W_, true, NB, BIG>), grid, block, p.lds_bytes, st, a); \
+        else hipLaunchKernelGGL((k_rec<W_, false, NB, BIG>), grid, block, p.lds_bytes, st, a);         \
+    }
+        TPL_REC_W(1)
+        TPL_REC_W(2)
+        TPL_REC_W(4)
+        TPL_REC_W(8)
+        TPL_REC_W(16)
+#undef TPL_REC_W
+        return hipGetLastError();
+    }
     case TPL_KERNEL_REG16: {
         Reg16Args a = p.reg16;
         a.src = src;
@@ -732,6 +826,7 @@ static const char* kernel_name(int k) {
     case TPL_KERNEL_REG16: return "reg16";
     case TPL_KERNEL_COPY: return "copy";
     case TPL_KERNEL_SWAP: return "swap";
+    case TPL_KERNEL_REC: return "rec";
     default: return "none";
     }
 }

@@ -376,6 +376,9 @@ static LdsChoice cached_choice(const LdsShape& sh) {
 // ---------------------------------------------------------------------------
 // Device plan.
 
+// The records kernel decomposes the batch modes only (at most the shard).
+static bool rank_ok_for_rec(const Shard& sh) { return sh.rank <= kMaxBatch + 2; }
+
 static int pow2_align(int64_t x) {
     // largest power of two (<= 256) dividing x (x == 0 counts as 256)
     int a = 1;
@@ -704,6 +707,48 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             p.lds_bytes = pick->tb * c.pitch;
             p.unit_is_item = (l.ntb == 1 && l.nta == 1 && mb.e == pick->tb && ma.e == pick->ta);
             return p;
+        }
+        // Records: the shorter of the two contiguous modes is a record of F
+        // fields that is dense on its side (records one after the other),
+        // the longer one counts records.  The dense side moves as one block.
+        if (plain && rank_ok_for_rec(sh)) {
+            const bool src_records = ma.e <= mb.e;   // records dense in the source
+            const Mode& mf = src_records ? ma : mb;    // field mode
+            const Mode& mr = src_records ? mb : ma;    // record mode
+            const int64_t F = mf.e;
+            const bool dense = src_records ? (mr.s == F) : (mr.d == F);
+            const int64_t fstride = src_records ? mf.d : mf.s;   // field rows on the sparse side
+            // 16-byte pieces on both sides of a full tile: base, batch strides
+            // and field rows aligned; the block start moves by TR F w bytes.
+            const bool aligned = sa % 16 == 0 && da % 16 == 0 && (fstride * w) % 16 == 0 &&
+                                 all_aligned(sh, a, b, w, true, 16) && all_aligned(sh, a, b, w, false, 16);
+            if (dense && F * w <= 1024 && aligned && mr.e >= ce) {
+                int64_t tr = 1;
+                while (tr * 2 * F * w <= 16384) tr *= 2;
+                tr = std::max<int64_t>(tr, ce);
+                tr = std::min<int64_t>(tr, mr.e / ce * ce);
+                p.kernel = TPL_KERNEL_REC;
+                p.rec_dense_src = src_records;
+                RecArgs& r = p.rec;
+                r.F = (int32_t)F;
+                r.TR = (int32_t)tr;
+                r.nrec = mr.e;
+                r.ntr = (mr.e + tr - 1) / tr;
+                r.div_ntr = make_fastdiv((uint32_t)std::min<int64_t>(r.ntr, 0x7fffffff));
+                r.fstride = fstride;
+                int64_t items = 1;
+                for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
+                r.ntiles = items * r.ntr;
+                if (r.ntiles >= ((int64_t)1 << 31)) p.big = true;
+                set_modes(r.batch, sh, others, no);
+                p.P = ce;
+                p.tile_b = src_records ? (int)tr : (int)F;
+                p.tile_a = src_records ? (int)F : (int)tr;
+                p.block = 256;
+                p.grid = r.ntiles;
+                p.lds_bytes = (int)(tr * F * w);
+                return p;
+            }
         }
     }
     choose_gather();

@@ -75,6 +75,8 @@ struct Plan {
     QuadArgs quad{};
     LdsArgs lds{};
     Reg16Args reg16{};
+    RecArgs rec{};
+    bool rec_dense_src = false;
 };
 
 // Full planning for the device path.  src_align / dst_align: alignment in

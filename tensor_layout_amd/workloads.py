@@ -81,6 +81,8 @@ SF_U8 = Workload("sf_transpose_2^20x4x32_u8", 1, (4, 32), (32, 1), (1, 4), batch
 SF_F16 = Workload("sf_transpose_2^20x4x32_f16", 2, (4, 32), (32, 1), (1, 4), batch=1 << 20, seed=_seed(2, 3))
 # An array of 2^24 float4 records to one array per component (AoS -> SoA).
 AOS_TO_SOA = Workload("aos_to_soa_2^24x4_f32", 4, (1 << 24, 4), (4, 1), (1, 1 << 24), seed=_seed(7))
+# An array of 2^24 float3 (xyz) records to 3 field arrays.
+AOS3_TO_SOA = Workload("aos_to_soa_2^24x3_f32", 4, (1 << 24, 3), (3, 1), (1, 1 << 24), seed=_seed(7, 1))
 # The SF transpose into XOR-swizzled destination tiles: the 16-byte chunk
 # index of each 128-element tile (bits 2..3 of the offset) is XORed with bits
 # 5..6; the swizzle period is one tile.
@@ -98,7 +100,7 @@ BF16_16K_INPLACE = Workload("transpose_16384x16384_bf16_inplace", 2, (16384, 163
 COPY_CALIBRATION = Workload("identity_copy_512MiB_u32", 4, (1 << 27,), (1,), (1,), seed=0x5EED0100)
 
 ALL = ([SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)]
-       + [BF16_16K, W16_4K, OUTER_PERM, SF_SWIZZLED, TILE_SWIZZLED, SF_U8, SF_F16, AOS_TO_SOA])
+       + [BF16_16K, W16_4K, OUTER_PERM, SF_SWIZZLED, TILE_SWIZZLED, SF_U8, SF_F16, AOS_TO_SOA, AOS3_TO_SOA])
 INPLACE = [BF16_16K_INPLACE]
 
 

@@ -154,6 +154,7 @@ EXPECTED_KERNEL = {
     "sf_transpose_2^20x4x32_u8": "quad",
     "sf_transpose_2^20x4x32_f16": "quad",
     "aos_to_soa_2^24x4_f32": "quad",
+    "aos_to_soa_2^24x3_f32": "rec",
 }
 
 

@@ -133,6 +133,14 @@ RAGGED = [
     ("quad_aos_to_soa_f16x8", 2, (40000, 8), (8, 1), (1, 40000), "quad"),
     ("quad_aos_to_soa_u8x16_batched", 1, (2, 8192, 16), (8192 * 16, 16, 1), (8192 * 16, 1, 8192), "quad"),
     ("quad_soa_to_aos_f16x8", 2, (8, 40000), (40000, 1), (1, 8), "quad"),
+    ("rec_aos_to_soa_f32x3", 4, (100003, 3), (3, 1), (1, 100004), "rec"),
+    ("rec_soa_to_aos_f32x3_batched", 4, (2, 3, 50000), (150000, 50000, 1), (150000, 1, 3), "rec"),
+    ("rec_rgb_to_planes", 1, (3, 65536, 3), (65536 * 3, 3, 1), (3 * 65536, 1, 65536), "rec"),
+    ("rec_planes_to_rgb", 1, (3, 70000), (70000, 1), (1, 3), "rec"),
+    ("rec_aos_to_soa_f32x17", 4, (4000, 17), (17, 1), (1, 4000), "rec"),
+    ("rec_aos_to_soa_f16x6", 2, (3, 9000, 6), (54000, 6, 1), (54000, 1, 9000), "rec"),
+    ("rec_aos_to_soa_u64x3", 8, (5000, 3), (3, 1), (1, 5000), "rec"),
+    ("rec_aos_to_soa_f32x2_short", 4, (5, 2), (2, 1), (1, 8), "rec"),
     ("quad_aos_to_soa_f32x4", 4, (100000, 4), (4, 1), (1, 100000), "quad"),
     ("quad_aos_to_soa_f32x8_batched", 4, (3, 4096, 8), (32768, 8, 1), (32768, 1, 4096), "quad"),
     ("quad_aos_to_soa_f32x12_padded", 4, (2000, 12), (16, 1), (1, 2048), "quad"),
@@ -142,7 +150,8 @@ RAGGED = [
     ("copy_identity", 2, (1000, 64), (64, 1), (64, 1), "copy"),
     ("copy_runs_of_8_bytes", 2, (40, 12), (12, 1), (480, 1), "copy"),
     ("copy_runs_of_4_bytes", 1, (3, 50, 4), (200, 4, 1), (4, 12, 1), "copy"),
-    ("gather_unaligned_rows", 2, (130, 1000), (1000, 1), (1, 130), "gather"),
+    ("rec_unaligned_rows_dense_dst", 2, (130, 1000), (1000, 1), (1, 130), "rec"),
+    ("gather_unaligned_rows_padded_dst", 2, (130, 1000), (1000, 1), (1, 131), "gather"),
     ("gather_no_unit_stride", 4, (16, 24), (48, 2), (24, 1), "gather"),
     ("gather_small_modes", 8, (3, 5, 7), (35, 7, 1), (1, 3, 15), "gather"),
     ("lds_broadcast_src", 4, (64, 32), (0, 1), (1, 64), "lds"),
@@ -152,7 +161,7 @@ RAGGED = [
 @pytest.mark.parametrize("case", RAGGED, ids=lambda c: c[0])
 def test_ragged_and_kernel_families(case):
     name, w, ext, ss, ds, kernel = case
-    batch = 3 if kernel not in ("lds",) else 1
+    batch = 3 if kernel not in ("lds", "rec") else 1
     run_case(name, w, ext, ss, ds, seed=zlib.crc32(name.encode()) & 0xFFFF, expect_kernel=kernel, batch=batch)
 
 

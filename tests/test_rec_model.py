@@ -1,0 +1,119 @@
+"""CPU model of the records kernel's index arithmetic (k_rec), run before the
+GPU does: for small layouts it replays every thread's accesses of both
+phases on numpy buffers, checks that each one stays inside the layout's
+footprint, and that the result equals the oracle's.  The model is written
+from the kernel's description (tile of TR records, LDS in record order,
+dense block on one side, 16-byte pieces of field rows on the other, element
+by element for a short last tile), not shared with it."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from tensor_layout_amd import synth, tpl
+
+NT = 256
+
+
+def model(x, w, ext, ss, ds, batch, dense_src, F, TR, nrec, fstride, batch_offsets):
+    """Replay k_rec; returns (output bytes, set of source and destination element offsets touched)."""
+    out = np.zeros(batch_offsets["dst_size"] * w, dtype=np.uint8)
+    touched_s, touched_d = set(), set()
+    ce = 16 // w
+    ntr = -(-nrec // TR)
+    for item, (so, d_o) in enumerate(batch_offsets["items"]):
+        for ti in range(ntr):
+            r0 = ti * TR
+            nr = min(TR, nrec - r0)
+            lds = {}
+            block = so + r0 * F if dense_src else d_o + r0 * F
+            rows = d_o + r0 if dense_src else so + r0
+            if nr == TR:
+                nq = TR // ce
+                nchunks = F * TR // ce
+                # phase 1
+                if dense_src:
+                    for c in range(nchunks):
+                        for k in range(ce):
+                            e = block + c * ce + k
+                            touched_s.add(e)
+                            lds[c * ce + k] = x[e * w:(e + 1) * w]
+                else:
+                    for g in range(nchunks):
+                        q, f = g % nq, g // nq
+                        for k in range(ce):
+                            e = rows + f * fstride + q * ce + k
+                            touched_s.add(e)
+                            lds[(q * ce + k) * F + f] = x[e * w:(e + 1) * w]
+                # phase 2
+                if dense_src:
+                    for g in range(nchunks):
+                        q, f = g % nq, g // nq
+                        for k in range(ce):
+                            e = rows + f * fstride + q * ce + k
+                            touched_d.add(e)
+                            out[e * w:(e + 1) * w] = lds[(q * ce + k) * F + f]
+                else:
+                    for c in range(nchunks):
+                        for k in range(ce):
+                            e = block + c * ce + k
+                            touched_d.add(e)
+                            out[e * w:(e + 1) * w] = lds[c * ce + k]
+            else:
+                for i in range(nr * F):
+                    f, r = i // nr, i % nr
+                    e = block + r * F + f if dense_src else rows + f * fstride + r
+                    touched_s.add(e)
+                    lds[r * F + f] = x[e * w:(e + 1) * w]
+                for i in range(nr * F):
+                    f, r = i // nr, i % nr
+                    e = rows + f * fstride + r if dense_src else block + r * F + f
+                    touched_d.add(e)
+                    out[e * w:(e + 1) * w] = lds[r * F + f]
+    return out, touched_s, touched_d
+
+
+def footprint(ext, strides, batch, span):
+    pts = {0}
+    for e, s in zip(ext, strides):
+        pts = {p + i * s for p in pts for i in range(e)}
+    return {b * span + p for b in range(batch) for p in pts}
+
+
+CASES = [
+    # w, extents, src strides, dst strides, batch
+    (4, (600, 3), (3, 1), (1, 600), 2),        # float3 records -> fields, a short last tile
+    (4, (3, 600), (600, 1), (1, 3), 2),        # and back
+    (1, (5000, 3), (3, 1), (1, 5008), 1),      # RGB -> planes (rows padded to 16 bytes)
+    (1, (3, 5000), (5008, 1), (1, 3), 1),      # planes -> RGB
+    (4, (200, 17), (17, 1), (1, 208), 1),      # 17-float records
+    (2, (1000, 6), (6, 1), (1, 1000), 3),
+    (8, (300, 3), (3, 1), (1, 300), 1),
+    (4, (5, 2), (2, 1), (1, 8), 1),            # one full tile of 4 records, one of 1
+    (2, (3, 2000), (2000, 1), (1, 3), 2),      # fp16 planes -> 3-field records
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"w{c[0]}_{c[1]}")
+def test_records_kernel_model(case):
+    w, ext, ss, ds, batch = case
+    p = tpl.tpl_plan(w, ext, ss, ds, batch=batch)
+    assert p.ok and p.kernel == "rec", p
+    src_records = ext[1] <= ext[0]
+    F = ext[1] if src_records else ext[0]
+    nrec = ext[0] if src_records else ext[1]
+    TR = p.tile[0] if src_records else p.tile[1]
+    fstride = ds[1] if src_records else ss[0]
+    assert TR % (16 // w) == 0 and TR <= nrec
+    span_s = 1 + sum((e - 1) * s for e, s in zip(ext, ss))
+    span_d = 1 + sum((e - 1) * s for e, s in zip(ext, ds))
+    x = synth.random_bytes(7, batch * span_s * w).copy()
+    ref = np.zeros(batch * span_d * w, dtype=np.uint8)
+    oracle.permute(x, ref, w, ext, ss, ds, (0, 0), batch)
+    offs = {"items": [(b * span_s, b * span_d) for b in range(batch)], "dst_size": batch * span_d}
+    out, ts, td = model(x, w, ext, ss, ds, batch, src_records, F, TR, nrec, fstride, offs)
+    assert ts <= footprint(ext, ss, batch, span_s)
+    assert td == footprint(ext, ds, batch, span_d)
+    assert np.array_equal(out, ref)
