@@ -525,18 +525,56 @@ __global__ void __launch_bounds__(T * T * W / (16 * CPT)) k_swap(LdsArgs a) {
 // ---------------------------------------------------------------------------
 // Records kernel (layouts whose short side is a whole record of F fields,
 // any F: float3 or RGB records to field arrays and back).  The tile holds
-// TR consecutive records in LDS in record order, element (r, f) at byte
-// (r F + f) W.  DENSE_SRC: the source tile is one contiguous block (records
-// one after the other), loaded as 16-byte chunks; every field's TR elements
-// then leave as 16-byte pieces of that field's destination row.  Otherwise
-// the mirror: 16-byte pieces of each field's source row in, the contiguous
-// destination block out.  A tile with fewer than TR records goes element
-// by element through the same LDS layout.
+// TR consecutive records in LDS in record order, byte b = (r F + f) W of
+// the tile's dense block in 16-byte chunk b / 16.  DENSE_SRC: the source
+// tile is one contiguous block (records one after the other), loaded as
+// 16-byte chunks; every field's TR elements then leave as 16-byte pieces of
+// that field's destination row.  Otherwise the mirror: 16-byte pieces of
+// each field's source row in, the contiguous destination block out.  A
+// tile with fewer than TR records goes element by element (plain record
+// order in both phases).
+//
+// Lane q of the piece phase touches record q CE + k, so neighbouring lanes
+// are 16 F bytes apart, a whole number of chunks: in plain record order
+// they share at most 8 of the 32 banks (4-way conflicts).  TURN places
+// chunk c turned by dwords (c / 8) mod 4 (elements of at most 4 bytes) or
+// by halves (c / 16) mod 2 (8-byte elements), which spreads lanes with
+// equal c mod 8 (resp. 16) over the other positions: no conflicts for odd
+// F, half of them for even F, and the chunk phase still moves whole
+// aligned chunks.  It pays only where the piece phase writes LDS with
+// elements of 4 bytes or more (fields to records: +5% for fp32); where the
+// piece phase reads, or elements are narrower, the slot arithmetic per
+// element costs more than the conflicts (up to -16% for bytes), so the
+// other instances keep plain record order.
+
+template <int W>
+__device__ __forceinline__ int rec_turn(int c) {   // bytes
+    constexpr int TM = W <= 4 ? 12 : W == 8 ? 8 : 0;
+    return (c >> 1) & TM;
+}
+
+template <int W, bool TURN>
+__device__ __forceinline__ int rec_slot(int b) {
+    if constexpr (!TURN) return b;
+    else return (b & ~15) | ((b + rec_turn<W>(b >> 4)) & 15);
+}
+
+// The contents of chunk c read back out of its (turned) slot.
+template <int W, bool TURN>
+__device__ __forceinline__ u32x4 rec_unturn(u32x4 v, int c) {
+    if constexpr (TURN) {
+        const int r = rec_turn<W>(c) >> 2;   // dwords
+        if (r & 1) v = v.yzwx;
+        if (r & 2) v = v.zwxy;
+    }
+    return v;
+}
 
 template <int W, bool DENSE_SRC, int NB, bool BIG>
 __global__ void __launch_bounds__(256) k_rec(RecArgs a) {
     constexpr int NT = 256;
     constexpr int CE = 16 / W;   // elements per 16-byte piece
+    constexpr bool TURN = !DENSE_SRC && W >= 4;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int t = threadIdx.x;
     const int F = a.F;
@@ -564,7 +602,8 @@ __global__ void __launch_bounds__(256) k_rec(RecArgs a) {
                     const u32x4 v = ld16(a.src + (rows + f * a.fstride + (int64_t)q * CE) * W);
                     const uint8_t* vb = reinterpret_cast<const uint8_t*>(&v);
 #pragma unroll
-                    for (int k = 0; k < CE; ++k) copy_elem<W>(lds + ((q * CE + k) * F + f) * W, vb + k * W);
+                    for (int k = 0; k < CE; ++k)
+                        copy_elem<W>(lds + rec_slot<W, TURN>(((q * CE + k) * F + f) * W), vb + k * W);
                 }
             }
             __syncthreads();
@@ -574,12 +613,14 @@ __global__ void __launch_bounds__(256) k_rec(RecArgs a) {
                     u32x4 v;
                     uint8_t* vb = reinterpret_cast<uint8_t*>(&v);
 #pragma unroll
-                    for (int k = 0; k < CE; ++k) copy_elem<W>(vb + k * W, lds + ((q * CE + k) * F + f) * W);
+                    for (int k = 0; k < CE; ++k)
+                        copy_elem<W>(vb + k * W, lds + rec_slot<W, TURN>(((q * CE + k) * F + f) * W));
                     st16(a.dst + (rows + f * a.fstride + (int64_t)q * CE) * W, v);
                 }
             } else {
                 for (int c = t; c < nchunks; c += NT)
-                    st16(a.dst + block * W + (int64_t)c * 16, *reinterpret_cast<const u32x4*>(lds + c * 16));
+                    st16(a.dst + block * W + (int64_t)c * 16,
+                         rec_unturn<W, TURN>(*reinterpret_cast<const u32x4*>(lds + c * 16), c));
             }
         } else {
             for (int i = t; i < nel; i += NT) {

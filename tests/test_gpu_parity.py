@@ -312,24 +312,81 @@ def test_repeatable():
     assert torch.equal(outs[0], outs[1])
 
 
-def test_big_index_path_sampled():
-    """More than 2^31 elements (64-bit index math): checked on sampled coordinates."""
+BIG_CASES = [
+    # name, w, extents, src strides, dst strides, batch, kernel
+    ("lds_u8_axes021", 1, (48, 65536, 704), (704 * 65536, 704, 1), (704 * 65536, 1, 65536), 1, "lds"),
+    ("quad_u8_sf", 1, (4, 32), (32, 1), (1, 4), 1 << 24, "quad"),
+    ("rec_rgb_to_planes", 1, (1 << 30, 3), (3, 1), (1, 1 << 30), 1, "rec"),
+    ("rec_planes_to_rgb", 1, (3, 3 << 28), (3 << 28, 1), (1, 3), 1, "rec"),
+    ("copy_u8_row_blocks", 1, (2, 1024, 1 << 20), (1 << 30, 1 << 20, 1), (1 << 20, 1 << 21, 1), 1, "copy"),
+    ("gather_u8_stride2", 1, (1 << 31,), (2,), (1,), 1, "gather"),
+]
+
+
+def sampled_pairs(ext, ss, ds, batch, seed, count=4096):
+    """Source and destination element indices of `count` random coordinates, by the oracle's address rule."""
+    span_s = 1 + sum((e - 1) * s for e, s in zip(ext, ss))
+    span_d = 1 + sum((e - 1) * s for e, s in zip(ext, ds))
+    rng = np.random.default_rng(seed)
+    coords = np.stack([rng.integers(0, e, count) for e in ext], axis=1)
+    items = rng.integers(0, batch, count)
+    si = [int(b) * span_s + oracle.address(tuple(int(v) for v in c), ss) for b, c in zip(items, coords)]
+    di = [int(b) * span_d + oracle.address(tuple(int(v) for v in c), ds) for b, c in zip(items, coords)]
+    return si, di, span_s, span_d
+
+
+@pytest.mark.parametrize("case", BIG_CASES, ids=lambda c: c[0])
+def test_big_index_paths_sampled(case):
+    """At least 2^31 elements (the kernels' 64-bit index instances): sampled
+    coordinates against the oracle's address rule, the whole result against
+    PyTorch's strided views of the same layouts, and no destination byte
+    left unwritten."""
     torch = _torch()
-    ext, ss, ds, w = (48, 65536, 704), (704 * 65536, 704, 1), (704 * 65536, 1, 65536), 1
-    n = 48 * 65536 * 704
+    name, w, ext, ss, ds, batch, kernel = case
+    n = batch
+    for e in ext:
+        n *= e
     assert n >= 1 << 31
-    plan = tpl.tpl_plan(w, ext, ss, ds)
-    print(f"\n[case] big index path: {n} elements, kernel {plan.kernel}", flush=True)
-    x = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=torch.Generator("cuda").manual_seed(5))
-    d = torch.full((n,), SENTINEL, dtype=torch.uint8, device="cuda")
-    tpl.permute(d, x, ext, ss, ds, dtype_bytes=w)
+    plan = tpl.tpl_plan(w, ext, ss, ds, batch=batch)
+    assert plan.kernel == kernel, plan
+    si, di, span_s, span_d = sampled_pairs(ext, ss, ds, batch, 11)
+    print(f"\n[case] big index path {name}: {n} elements, kernel {plan.kernel}", flush=True)
+    gen = torch.Generator("cuda").manual_seed(5)
+    x = torch.randint(0, 256, (batch * span_s,), dtype=torch.uint8, device="cuda", generator=gen)
+    d = torch.full((batch * span_d,), SENTINEL, dtype=torch.uint8, device="cuda")
+    tpl.permute(d, x, ext, ss, ds, batch=batch, dtype_bytes=w)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(11)
-    coords = np.stack([rng.integers(0, e, 4096) for e in ext], axis=1)
-    src_idx = [oracle.address(tuple(int(v) for v in c), ss) for c in coords]
-    dst_idx = [oracle.address(tuple(int(v) for v in c), ds) for c in coords]
-    xs = x[torch.tensor(src_idx, device="cuda")].cpu().numpy()
-    ys = d[torch.tensor(dst_idx, device="cuda")].cpu().numpy()
+    xs = x[torch.tensor(si, device="cuda")].cpu().numpy()
+    ys = d[torch.tensor(di, device="cuda")].cpu().numpy()
     assert np.array_equal(xs, ys)
-    # every destination byte was written (no sentinel left where the sample says data)
-    assert int((d == SENTINEL).sum()) == int((x == SENTINEL).sum())
+    bs, bd = (span_s,), (span_d,)
+    src_view = torch.as_strided(x, (batch,) + tuple(ext), bs + tuple(ss))
+    dst_view = torch.as_strided(d, (batch,) + tuple(ext), bd + tuple(ds))
+    assert torch.equal(src_view, dst_view)
+    # every destination element is covered by the layout, so a byte still
+    # holding the sentinel must hold it in the source too
+    assert int((d == SENTINEL).sum()) == int((src_view == SENTINEL).sum())
+    del x, d, src_view, dst_view
+    torch.cuda.empty_cache()
+
+
+def test_big_in_place_transpose_sampled():
+    """A 65536 x 65536 byte matrix (2^32 elements) transposed in place by the
+    tile-pair swap kernel's 64-bit instance."""
+    torch = _torch()
+    ext, ss, ds = (65536, 65536), (65536, 1), (1, 65536)
+    plan = tpl.tpl_plan(1, ext, ss, ds, geometry=tpl.TPL_GEOM_GFX950_INPLACE)
+    assert plan.kernel == "swap", plan
+    si, di, _, _ = sampled_pairs(ext, ss, ds, 1, 13)
+    print("\n[case] big in-place transpose 65536x65536 u8, kernel swap", flush=True)
+    gen = torch.Generator("cuda").manual_seed(6)
+    buf = torch.randint(0, 256, (1 << 32,), dtype=torch.uint8, device="cuda", generator=gen)
+    x0 = buf.clone()
+    tpl.permute(buf, buf, ext, ss, ds, dtype_bytes=1)
+    torch.cuda.synchronize()
+    xs = x0[torch.tensor(si, device="cuda")].cpu().numpy()
+    ys = buf[torch.tensor(di, device="cuda")].cpu().numpy()
+    assert np.array_equal(xs, ys)
+    assert torch.equal(buf.view(65536, 65536), x0.view(65536, 65536).t())
+    del buf, x0
+    torch.cuda.empty_cache()

@@ -2,9 +2,13 @@
 GPU does: for small layouts it replays every thread's accesses of both
 phases on numpy buffers, checks that each one stays inside the layout's
 footprint, and that the result equals the oracle's.  The model is written
-from the kernel's description (tile of TR records, LDS in record order,
-dense block on one side, 16-byte pieces of field rows on the other, element
-by element for a short last tile), not shared with it."""
+from the kernel's description (tile of TR records, LDS in record order --
+for fields to records with elements of 4 bytes or more, each 16-byte chunk
+turned by whole dwords or halves -- dense block on one side, 16-byte pieces
+of field rows on the other, element by element for a short last tile), not
+shared with it.  LDS is a byte array here, so a chunk turned one way on the
+chunk side and read another way on the piece side shows up as a wrong
+result."""
 
 from __future__ import annotations
 
@@ -17,17 +21,51 @@ from tensor_layout_amd import synth, tpl
 NT = 256
 
 
+def turn_dwords(w, c, turned=True):
+    """Dword positions chunk c of a full tile is turned by in LDS."""
+    if not turned:
+        return 0
+    if w <= 4:
+        return (c // 8) % 4
+    if w == 8:
+        return 2 * ((c // 16) % 2)
+    return 0
+
+
+def chunk_into_lds(lds, c, data, w, turned):
+    r = turn_dwords(w, c, turned)
+    for j in range(4):
+        pos = (j + r) % 4
+        lds[c * 16 + pos * 4:c * 16 + pos * 4 + 4] = data[j * 4:j * 4 + 4]
+
+
+def chunk_from_lds(lds, c, w, turned):
+    r = turn_dwords(w, c, turned)
+    out = np.zeros(16, dtype=np.uint8)
+    for j in range(4):
+        pos = (j + r) % 4
+        out[j * 4:j * 4 + 4] = lds[c * 16 + pos * 4:c * 16 + pos * 4 + 4]
+    return out
+
+
+def elem_slot(b, w, turned=True):
+    """LDS byte of element byte b of a full tile's dense block."""
+    c, off = divmod(b, 16)
+    return c * 16 + (off + 4 * turn_dwords(w, c, turned)) % 16
+
+
 def model(x, w, ext, ss, ds, batch, dense_src, F, TR, nrec, fstride, batch_offsets):
     """Replay k_rec; returns (output bytes, set of source and destination element offsets touched)."""
     out = np.zeros(batch_offsets["dst_size"] * w, dtype=np.uint8)
     touched_s, touched_d = set(), set()
     ce = 16 // w
+    turned = not dense_src and w >= 4
     ntr = -(-nrec // TR)
     for item, (so, d_o) in enumerate(batch_offsets["items"]):
         for ti in range(ntr):
             r0 = ti * TR
             nr = min(TR, nrec - r0)
-            lds = {}
+            lds = np.full(TR * F * w, 0xEE, dtype=np.uint8)
             block = so + r0 * F if dense_src else d_o + r0 * F
             rows = d_o + r0 if dense_src else so + r0
             if nr == TR:
@@ -36,17 +74,17 @@ def model(x, w, ext, ss, ds, batch, dense_src, F, TR, nrec, fstride, batch_offse
                 # phase 1
                 if dense_src:
                     for c in range(nchunks):
-                        for k in range(ce):
-                            e = block + c * ce + k
-                            touched_s.add(e)
-                            lds[c * ce + k] = x[e * w:(e + 1) * w]
+                        e0 = block + c * ce
+                        touched_s.update(range(e0, e0 + ce))
+                        chunk_into_lds(lds, c, x[e0 * w:(e0 + ce) * w], w, turned)
                 else:
                     for g in range(nchunks):
                         q, f = g % nq, g // nq
                         for k in range(ce):
                             e = rows + f * fstride + q * ce + k
                             touched_s.add(e)
-                            lds[(q * ce + k) * F + f] = x[e * w:(e + 1) * w]
+                            sl = elem_slot(((q * ce + k) * F + f) * w, w, turned)
+                            lds[sl:sl + w] = x[e * w:(e + 1) * w]
                 # phase 2
                 if dense_src:
                     for g in range(nchunks):
@@ -54,24 +92,24 @@ def model(x, w, ext, ss, ds, batch, dense_src, F, TR, nrec, fstride, batch_offse
                         for k in range(ce):
                             e = rows + f * fstride + q * ce + k
                             touched_d.add(e)
-                            out[e * w:(e + 1) * w] = lds[(q * ce + k) * F + f]
+                            sl = elem_slot(((q * ce + k) * F + f) * w, w, turned)
+                            out[e * w:(e + 1) * w] = lds[sl:sl + w]
                 else:
                     for c in range(nchunks):
-                        for k in range(ce):
-                            e = block + c * ce + k
-                            touched_d.add(e)
-                            out[e * w:(e + 1) * w] = lds[c * ce + k]
+                        e0 = block + c * ce
+                        touched_d.update(range(e0, e0 + ce))
+                        out[e0 * w:(e0 + ce) * w] = chunk_from_lds(lds, c, w, turned)
             else:
                 for i in range(nr * F):
                     f, r = i // nr, i % nr
                     e = block + r * F + f if dense_src else rows + f * fstride + r
                     touched_s.add(e)
-                    lds[r * F + f] = x[e * w:(e + 1) * w]
+                    lds[(r * F + f) * w:(r * F + f + 1) * w] = x[e * w:(e + 1) * w]
                 for i in range(nr * F):
                     f, r = i // nr, i % nr
                     e = rows + f * fstride + r if dense_src else block + r * F + f
                     touched_d.add(e)
-                    out[e * w:(e + 1) * w] = lds[r * F + f]
+                    out[e * w:(e + 1) * w] = lds[(r * F + f) * w:(r * F + f + 1) * w]
     return out, touched_s, touched_d
 
 
@@ -93,7 +131,16 @@ CASES = [
     (8, (300, 3), (3, 1), (1, 300), 1),
     (4, (5, 2), (2, 1), (1, 8), 1),            # one full tile of 4 records, one of 1
     (2, (3, 2000), (2000, 1), (1, 3), 2),      # fp16 planes -> 3-field records
+    (8, (3, 700), (700, 1), (1, 3), 1),        # 8-byte fields to records: chunks turned by halves
+    (4, (5, 900), (900, 1), (1, 5), 1),        # fp32 fields to records: chunks turned by dwords
+    (1, (6, 4000), (4000, 1), (1, 6), 1),      # even field count
 ]
+
+
+def test_turn_is_a_permutation_of_each_chunk():
+    for w in (1, 2, 4, 8, 16):
+        for c in range(64):
+            assert sorted(elem_slot(c * 16 + o, w) - c * 16 for o in range(0, 16, 4)) == [0, 4, 8, 12]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"w{c[0]}_{c[1]}")
@@ -117,3 +164,24 @@ def test_records_kernel_model(case):
     assert ts <= footprint(ext, ss, batch, span_s)
     assert td == footprint(ext, ds, batch, span_d)
     assert np.array_equal(out, ref)
+
+
+@pytest.mark.parametrize("w", [1, 2, 4, 8])
+@pytest.mark.parametrize("F", [3, 5, 7, 17])
+def test_turn_spreads_piece_lanes_over_all_banks(w, F):
+    """Turned layout, piece phase, odd F: the 32 lanes of one LDS pass (consecutive q, same k
+    and f) touch 32 different banks -- 4-byte banks, 32 per 128 bytes for
+    accesses of up to a dword, 64 per 256 bytes for 8-byte ones.  In plain
+    record order they would share 8 (4-way conflicts)."""
+    ce = 16 // w
+    nbanks = 32 if w <= 4 else 64
+    for k in range(ce):
+        for f in range(F):
+            for q0 in (0, 32, 64):
+                banks = [elem_slot(((q * ce + k) * F + f) * w, w) // 4 % nbanks for q in range(q0, q0 + 32)]
+                if w == 8:
+                    assert len(set(banks)) == 32 and all(b % 2 == banks[0] % 2 for b in banks)
+                else:
+                    assert len(set(banks)) == 32
+                plain = [((q * ce + k) * F + f) * w // 4 % nbanks for q in range(q0, q0 + 32)]
+                assert len(set(plain)) <= 16
