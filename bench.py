@@ -105,6 +105,24 @@ def make_input(wl):
     return x
 
 
+def host_info():
+    """Host CPU model and the CPU count the process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
+
+
 def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
     """The oracle as it stands, single-threaded, on the full workload."""
     import numpy as np
@@ -127,6 +145,7 @@ def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
         "kind": "oracle",
         "sample": f"the full workload ({wl.elements} elements) permuted {runs} times by the "
                   f"single-threaded C oracle in {el:.1f} s",
+        "host": host_info(),
     }, y
 
 
@@ -253,6 +272,20 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
     elapsed = t1 - t0
     value = wl.bytes_moved * steps / elapsed / 1e9
     achieved = wl.bytes_moved / (avg_ms * 1e-3) / 1e9
+    # A second, shorter pass with an event pair around every launch: the
+    # spread of single launches (median, min, max).  Each interval also
+    # holds one event packet, so these read a little above the mean above.
+    nper = min(steps, 100)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nper)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        launch(warmup + steps + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in evs)
+    per_launch = {"launches": nper, "median_ms": round(per[nper // 2], 5), "min_ms": round(per[0], 5),
+                  "max_ms": round(per[-1], 5),
+                  "median_gbps": round(wl.bytes_moved / (per[nper // 2] * 1e-3) / 1e9, 2)}
 
 
     out = {
@@ -291,6 +324,7 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
             "lds_counters": lds_counters_for(wl.name),
             "kernel_ms_avg": round(avg_ms, 5),
             "host_enqueue_us": round(host_us, 2),
+            "per_launch": per_launch,
         },
     }
     ref = None
@@ -311,7 +345,7 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
                 raise tpl.TplError(st, tpl.tpl_last_error())
             got = buf.cpu().numpy()
         else:
-            last = (warmup + steps - 1) % pairs
+            last = (warmup + steps + nper - 1) % pairs
             got = dsts[last].cpu().numpy()
         out["bitexact"] = bool(np.array_equal(got, ref))
     # Reference, after the check (it overwrites the outputs): a plain copy of

@@ -144,6 +144,10 @@ struct QuadArgs {
     Swz zs, zd;          // operand swizzles (byte form)
 };
 
+// In-place pair swaps walk tile pairs in blocks of kSwapG x kSwapG tiles.
+constexpr int kSwapLogG = 3;
+constexpr int kSwapG = 1 << kSwapLogG;
+
 struct LdsArgs {
     const uint8_t* src;
     uint8_t* dst;
@@ -155,10 +159,13 @@ struct LdsArgs {
     Modes batch;
     int32_t pitch;       // LDS row pitch, bytes
     int32_t shift_r, mask_r, shift_w, mask_w;
-    // In-place pair swaps only: tile pairs per batch item, and whether every
-    // tile goes element by element (bases or pitches not 16-byte aligned).
+    // In-place pair swaps only: work units per batch item, blocks of
+    // kSwapG x kSwapG tiles per side, and whether every tile goes element by
+    // element (bases or pitches not 16-byte aligned).
     int64_t npair;
     FastDiv div_npair;
+    int64_t nbl;
+    FastDiv div_nbl;
     int32_t scalar;
     Swz zs, zd;          // operand swizzles (byte form)
 };

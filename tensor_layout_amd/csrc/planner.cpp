@@ -920,8 +920,10 @@ Plan plan_inplace(int w, int rank, const int64_t* ext, const int64_t* ss, const 
     l.s_b = mb.s;
     l.d_a = ma.d;
     l.ntb = l.nta = (ma.e + T - 1) / T;
-    l.npair = (l.ntb / 2 + 1) * l.ntb;   // units per item (diagonal order, see k_swap)
-    l.div_ntb = make_fastdiv((uint32_t)std::min<int64_t>(l.ntb, 0x7fffffff));
+    // units per item: (M/2 + 1) M block units of G x G pairs (block order, see k_swap)
+    l.nbl = (l.ntb + kSwapG - 1) / kSwapG;
+    l.npair = (l.nbl / 2 + 1) * l.nbl * kSwapG * kSwapG;
+    l.div_nbl = make_fastdiv((uint32_t)std::min<int64_t>(l.nbl, 0x7fffffff));
     int64_t items = 1;
     for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
     l.ntiles = items * l.npair;

@@ -334,9 +334,47 @@ def test_inplace_square_transpose_plans_pair_swaps(w, T):
     p = tpl.tpl_plan(w, (n, n), (n, 1), (1, n), geometry=G_IN)
     assert p.ok and p.kernel == "swap" and p.tile == (T, T)
     m = -(-n // T)
-    assert p.grid == (m // 2 + 1) * m          # tile pairs c <= r in diagonal rows of m units
+    M = -(-m // SWAP_G)
+    assert p.grid == (M // 2 + 1) * M * SWAP_G ** 2   # blocks of 8 x 8 tile pairs, folded block diagonals
     q = tpl.tpl_plan(w, (3, n, n), (n * n + 64, n, 1), (n * n + 64, 1, n), geometry=G_IN)
     assert q.ok and q.kernel == "swap" and q.grid == 3 * p.grid
+
+
+SWAP_G = 8
+
+
+def swap_unit_pairs(m, units):
+    """CPU model of the in-place kernel's unit order: unit -> tile pair
+    (c, r), or None where the unit does nothing.  Written from the kernel's
+    description: G x G tile blocks, block pairs on folded block diagonals,
+    each block pair's G x G tile pairs, u <= v on the block diagonal."""
+    M = -(-m // SWAP_G)
+    out = []
+    for pr in range(units):
+        bu, rest = divmod(pr, SWAP_G * SWAP_G)
+        u, v = divmod(rest, SWAP_G)
+        kb, jb = divmod(bu, M)
+        if jb < M - kb:
+            db, cb = kb, jb
+        else:
+            db, cb = M - kb, jb - (M - kb)
+            if db == kb:
+                out.append(None)
+                continue
+        c, r = cb * SWAP_G + u, (cb + db) * SWAP_G + v
+        out.append(None if (db == 0 and u > v) or r >= m else (c, r))
+    return out
+
+
+@pytest.mark.parametrize("n", [16, 100, 1000, 2048, 5000])
+def test_inplace_unit_order_covers_every_tile_pair_once(n):
+    """Every unordered tile pair {c, r} (c == r: a tile with itself) is one
+    unit's work exactly once, so each tile is read and written once."""
+    p = tpl.tpl_plan(2, (n, n), (n, 1), (1, n), geometry=G_IN)
+    m = -(-n // p.tile[0])
+    got = [x for x in swap_unit_pairs(m, p.grid) if x is not None]
+    assert len(got) == len(set(got))
+    assert set(got) == {(c, r) for c in range(m) for r in range(c, m)}
 
 
 def test_inplace_keeps_read_before_write_kernels():
