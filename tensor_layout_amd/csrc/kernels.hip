@@ -603,8 +603,24 @@ __global__ void __launch_bounds__(256) k_rec(RecArgs a) {
             const int nchunks = nel * W / 16;    // == F * TR / CE
             const int nq = a.TR / CE;            // pieces per field row
             if constexpr (DENSE_SRC) {
-                for (int c = t; c < nchunks; c += NT)
-                    *reinterpret_cast<u32x4*>(lds + c * 16) = ld16(a.src + block * W + (int64_t)c * 16);
+                // Four chunk loads in flight per lane before their LDS writes
+                // (a plain loop waits on each load): +10% on float3 records,
+                // neutral for bytes.  The mirror direction measured faster
+                // with one piece at a time.
+                constexpr int U = 4;
+                for (int c0 = 0; c0 < nchunks; c0 += U * NT) {
+                    u32x4 v[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int c = c0 + u * NT + t;
+                        if (c < nchunks) v[u] = ld16(a.src + block * W + (int64_t)c * 16);
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int c = c0 + u * NT + t;
+                        if (c < nchunks) *reinterpret_cast<u32x4*>(lds + c * 16) = v[u];
+                    }
+                }
             } else {
                 for (int g = t; g < nchunks; g += NT) {
                     const int q = g % nq, f = g / nq;

@@ -70,6 +70,11 @@ CASES = [
     ("16B_100_ragged", 16, 100, 100, 1, 0, 0),
     ("16B_512", 16, 512, 512, 1, 0, 0),
     ("u16_65_batched_gap", 2, 65, 72, 4, 9, 0),
+    # tile counts past one 8 x 8-tile block: 10 (2 blocks, the second partly
+    # outside), 21 (3 blocks, ragged tiles), 40 (5 blocks, batched)
+    ("u8_1200_two_blocks", 1, 1200, 1200, 1, 0, 0),
+    ("16B_330_three_blocks_ragged", 16, 330, 330, 1, 0, 0),
+    ("u16_2560_five_blocks_batched", 2, 2560, 2560, 2, 64, 0),
 ]
 
 
