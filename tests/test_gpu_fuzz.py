@@ -13,6 +13,7 @@ import pytest
 import oracle
 from tensor_layout_amd import synth, tpl
 from tests.test_gpu_parity import run_case, make_input, sizes, SENTINEL
+from tests.test_gpu_inplace import run_inplace
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +72,66 @@ def test_random_permutations_match_oracle():
         run_case(f"fuzz_{t}", w, ext, ss, ds, offs, batch, seed=t, zs=zs, zd=zd)
     print("kernel mix:", dict(kernels), flush=True)
     assert {"lds", "gather", "copy", "quad"} <= set(kernels)
+
+
+def record_case(rng):
+    """Records of F fields (2..20) to one row per field, or back; rows mostly
+    padded to whole 16-byte pieces, some ragged or misaligned."""
+    w = int(rng.choice([1, 2, 4, 8, 16]))
+    F = int(rng.integers(2, 21))
+    while F * w > 1024:
+        F //= 2
+    N = int(rng.choice([int(rng.integers(1, 64)), int(rng.integers(64, 6000)), int(rng.integers(64, 6000))]))
+    align = max(1, 16 // w)
+    N = N if rng.random() < 0.3 else -(-N // align) * align
+    pad = int(rng.choice([0, 0, align, 3]))
+    rowlen = N + pad
+    batch = int(rng.choice([1, 1, 2, 3]))
+    if rng.random() < 0.5:
+        ext, ss, ds = (N, F), (F, 1), (1, rowlen)
+    else:
+        ext, ss, ds = (F, N), (rowlen, 1), (1, F)
+    offs = (int(rng.choice([0, 0, 0, align, 1])), int(rng.choice([0, 0, 0, 2 * align, 2])))
+    return w, ext, ss, ds, offs, batch
+
+
+def test_random_record_layouts_match_oracle():
+    rng = np.random.default_rng(7)
+    kernels = collections.Counter()
+    for t in range(60):
+        w, ext, ss, ds, offs, batch = record_case(rng)
+        p = tpl.tpl_plan(w, ext, ss, ds, offs, batch)
+        assert p.ok, (t, p)
+        kernels[p.kernel] += 1
+        run_case(f"records_{t}", w, ext, ss, ds, offs, batch, seed=100 + t)
+    print("kernel mix:", dict(kernels), flush=True)
+    assert kernels["rec"] >= 10
+
+
+def test_random_inplace_transposes_match_oracle():
+    """Square transposes in place: widths, sizes from one tile to eleven
+    8 x 8-tile blocks per side, padded or unaligned pitches, batches and
+    offsets."""
+    rng = np.random.default_rng(8)
+    kernels = collections.Counter()
+    for t in range(40):
+        w = int(rng.choice([1, 2, 4, 8, 16]))
+        n = int(rng.choice([int(rng.integers(1, 40)), int(rng.integers(40, 900)),
+                            int(rng.integers(900, 3000 if w <= 2 else 1500))]))
+        pitch = n + int(rng.choice([0, 0, 0, 3, 16]))
+        batch = int(rng.choice([1, 1, 2]))
+        gap = int(rng.choice([0, 8])) if batch > 1 else 0
+        offset = int(rng.choice([0, 0, 16, 1]))
+        item = n * pitch + gap
+        ext = (batch, n, n) if batch > 1 else (n, n)
+        ss = (item, pitch, 1) if batch > 1 else (pitch, 1)
+        ds = (item, 1, pitch) if batch > 1 else (1, pitch)
+        p = tpl.tpl_plan(w, ext, ss, ds, (offset, offset), 1, geometry=tpl.TPL_GEOM_GFX950_INPLACE)
+        assert p.ok, (t, p)
+        kernels[p.kernel] += 1
+        run_inplace(f"inplace_{t}", w, n, pitch, batch, gap, offset, seed=200 + t, expect_kernel=p.kernel)
+    print("kernel mix:", dict(kernels), flush=True)
+    assert kernels["swap"] >= 30
 
 
 def test_graph_capture_and_replay():
