@@ -63,7 +63,9 @@ enum {
 enum {
     TPL_KERNEL_NONE = 0,   /* nothing to do (empty tensor) or a PAGES32 plan */
     TPL_KERNEL_GATHER = 1, /* element-wise gather/scatter, any layout */
-    TPL_KERNEL_QUAD = 2,   /* 4x4 fp32 blocks transposed in registers by lane quads (DPP) */
+    TPL_KERNEL_QUAD = 2,   /* 4x4 dword blocks transposed in registers across lanes (DPP,
+                              permlane16 swap); 1-, 2- and 4-byte elements, a destination-
+                              contiguous extent of 4 (or 4-row blocks of records) */
     TPL_KERNEL_LDS = 3,    /* tiled 2-D transpose staged through LDS with XOR-ordered phases */
     TPL_KERNEL_REG16 = 4,  /* 16-byte elements: 8x8 element blocks, pure lane remap */
     TPL_KERNEL_COPY = 5,   /* both sides contiguous along one mode: vector copy of runs */
@@ -104,7 +106,9 @@ typedef struct {
                                        exchange's read phase (PAGES32: of both phases) */
     int32_t k_w, shift_w, mask_w;   /* GFX950 LDS kernel: XOR of the LDS write phase */
     int32_t kernel;                 /* TPL_KERNEL_* (GFX950 only) */
-    int32_t tile[2];                /* tile extents (b, a) in elements, LDS/QUAD kernels */
+    int32_t tile[2];                /* tile extents in elements along (b, a), the destination-
+                                       and the source-contiguous mode: LDS, SWAP, QUAD and REC
+                                       kernels */
     int32_t chunks_per_thread;      /* 16-byte source chunks each thread loads, LDS kernel */
     int32_t lds_pitch;              /* LDS row pitch in bytes, LDS kernel */
     int64_t grid, block;            /* launch shape of the main kernel */
