@@ -60,6 +60,23 @@ def traffic_for(name: str):
     return int(rec["fetch_bytes"] + rec["write_bytes"])
 
 
+def traffic_split_for(name: str):
+    """The same counters split into HBM reads and writes, with their sum over
+    the algorithmic bytes, or None when absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_hash():
+        return None
+    rec = t.get("workloads", {}).get(name)
+    if not rec:
+        return None
+    return {"read_bytes": int(rec["fetch_bytes"]), "write_bytes": int(rec["write_bytes"]),
+            "over_algorithmic": round((rec["fetch_bytes"] + rec["write_bytes"]) / rec["algorithmic_bytes"], 4)}
+
+
 def lds_counters_for(name: str):
     """Per-dispatch LDS counters of the dominant kernel (rocprofv3), or None
     when absent or taken on other kernel sources."""
@@ -321,6 +338,7 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4),
             "traffic": traffic_for(wl.name),
+            "traffic_split": traffic_split_for(wl.name),
             "lds_counters": lds_counters_for(wl.name),
             "kernel_ms_avg": round(avg_ms, 5),
             "host_enqueue_us": round(host_us, 2),
@@ -395,6 +413,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="sf_transpose_2^20x4x32_f32")
     ap.add_argument("--all", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--rounds", type=int, default=1,
+                    help="with --all: run the workloads interleaved this many rounds, drop the first "
+                         "round (when more than one) and report each workload's median round")
     ap.add_argument("--with-calibration", action="store_true",
                     help="with --all: also run the 512 MiB identity copy used to scale HBM counters")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -419,9 +440,38 @@ def main():
     by_name = {w.name: w for w in workloads.ALL + workloads.INPLACE + [workloads.COPY_CALIBRATION]}
     if a.all:
         todo = workloads.ALL + workloads.INPLACE + ([workloads.COPY_CALIBRATION] if a.with_calibration else [])
+        if a.rounds <= 1:
+            for wl in todo:
+                print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify,
+                                           do_ceiling=not a.no_ceiling)), flush=True)
+            return
+        # Rounds over all workloads in turn; the first round only warms the
+        # machine up.  Outputs are checked in the last round.
+        kept = {wl.name: [] for wl in todo}
+        for r in range(a.rounds):
+            last = r == a.rounds - 1
+            for wl in todo:
+                out = bench_one(wl, a.steps, a.warmup, False, last and not a.no_verify,
+                                do_ceiling=last and not a.no_ceiling)
+                print(f"round {r + 1}/{a.rounds} {wl.name}: {out['roofline']['achieved']} GB/s",
+                      file=sys.stderr, flush=True)
+                if r > 0:
+                    kept[wl.name].append(out)
         for wl in todo:
-            print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify,
-                                       do_ceiling=not a.no_ceiling)), flush=True)
+            outs = sorted(kept[wl.name], key=lambda o: o["roofline"]["achieved"])
+            med = dict(outs[len(outs) // 2])
+            final = kept[wl.name][-1]
+            for key in ("bitexact",):
+                if key in final:
+                    med[key] = final[key]
+            roof = dict(med["roofline"])
+            if final["roofline"].get("copy_ceiling_gbps"):
+                roof["copy_ceiling_gbps"] = final["roofline"]["copy_ceiling_gbps"]
+                roof["frac_of_copy_ceiling"] = round(roof["achieved"] / roof["copy_ceiling_gbps"], 4)
+            roof["rounds"] = {"kept": len(outs), "dropped": 1,
+                              "achieved_gbps": [o["roofline"]["achieved"] for o in kept[wl.name]]}
+            med["roofline"] = roof
+            print(json.dumps(med), flush=True)
         return
     wl = by_name[a.workload]
     print(json.dumps(bench_one(wl, a.steps, a.warmup, not a.no_cpu, not a.no_verify, a.entry, a.xor_k,
