@@ -62,29 +62,53 @@ __device__ __forceinline__ void project(const Shard& sh, int n, int* so, int* d_
     *d_o = d;
 }
 
-/* One 32-lane group permutes src into dst (element type T, P elements per
- * lane).  lane is the lane index inside the group (0..31). */
-template <typename T, int P>
-__device__ __forceinline__ void group_permute(T* dst, const T* src, const Shard& sh, int lane, int shift,
-                                              int mask, Swizzle zs = Swizzle{0, 0}, Swizzle zd = Swizzle{0, 0}) {
-    T regs[P];
+/* A lane's element offsets for its P iterations on both sides, in the order
+ * the program visits them (step r: iteration lane + 32 * (r ^ key)), with
+ * the sides' swizzles applied.  They depend only on the shard, the lane and
+ * the XOR, so a kernel that moves many regions with one layout computes them
+ * once and reuses them for every region. */
+template <int P>
+struct Offsets {
+    int src[P];
+    int dst[P];
+};
+
+template <int P>
+__device__ __forceinline__ Offsets<P> group_offsets(const Shard& sh, int lane, int shift, int mask,
+                                                    Swizzle zs = Swizzle{0, 0}, Swizzle zd = Swizzle{0, 0}) {
+    Offsets<P> o;
     const int key = (lane >> shift) & mask;
 #pragma unroll
     for (int r = 0; r < P; ++r) {
         int so, d_o;
         project(sh, lane + (r ^ key) * 32, &so, &d_o);
-        regs[r] = src[swizzle(zs, so)];
+        o.src[r] = swizzle(zs, so);
+        o.dst[r] = swizzle(zd, d_o);
     }
+    return o;
+}
+
+/* One 32-lane group permutes src into dst (element type T, P elements per
+ * lane) with offsets from group_offsets. */
+template <typename T, int P>
+__device__ __forceinline__ void group_permute(T* dst, const T* src, const Offsets<P>& o) {
+    T regs[P];
+#pragma unroll
+    for (int r = 0; r < P; ++r) regs[r] = src[o.src[r]];
     // Every lane's reads are issued, and their data consumed below, before any
     // write of this wave reaches LDS: in-place operands are safe.
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int r = 0; r < P; ++r) {
-        int so, d_o;
-        project(sh, lane + (r ^ key) * 32, &so, &d_o);
-        dst[swizzle(zd, d_o)] = regs[r];
-    }
+    for (int r = 0; r < P; ++r) dst[o.dst[r]] = regs[r];
     __builtin_amdgcn_wave_barrier();
+}
+
+/* The same for a single region: offsets computed on the spot.  lane is the
+ * lane index inside the group (0..31). */
+template <typename T, int P>
+__device__ __forceinline__ void group_permute(T* dst, const T* src, const Shard& sh, int lane, int shift,
+                                              int mask, Swizzle zs = Swizzle{0, 0}, Swizzle zd = Swizzle{0, 0}) {
+    group_permute<T, P>(dst, src, group_offsets<P>(sh, lane, shift, mask, zs, zd));
 }
 
 }  // namespace tpl_wave
