@@ -265,6 +265,39 @@ def _swz_reach(n_elems, z):
     return ((n_elems - 1) | ((1 << (z[1] + z[0])) - 1)) + 1
 
 
+def copy_view(dst, src, stream=None) -> None:
+    """Copy the strided tensor view ``src`` into the view ``dst`` (same shape
+    and dtype): every element lands where ``dst``'s own strides put it, as
+    ``dst[i, j, ...] = src[i, j, ...]``.  The layouts are the views' sizes
+    and strides, the bases their data pointers (storage offsets included),
+    so transposed, permuted, sliced and broadcast (stride-0) sources and
+    transposed or sliced destinations all map onto one tpl_permute call.
+    Size-1 dimensions are dropped (they move no address).  A destination
+    that overlaps the source is the library's case: a square transpose onto
+    itself runs in place, other overlaps raise TplError(TPL_E_ALIAS).
+    Raises TplError on any non-OK status."""
+    import torch
+
+    if tuple(src.shape) != tuple(dst.shape):
+        raise TplError(TPL_E_EXTENT, "extent mismatch")
+    if src.dtype != dst.dtype:
+        raise TplError(TPL_E_DTYPE, "dtype mismatch")
+    if not (src.is_cuda and dst.is_cuda):
+        raise TplError(TPL_E_ARG, "tensors must live on the GPU")
+    dims = [i for i, e in enumerate(src.shape) if e != 1]
+    if src.numel() == 0:
+        return
+    ext = tuple(int(src.shape[i]) for i in dims) or (1,)
+    ss = tuple(int(src.stride(i)) for i in dims) or (1,)
+    ds = tuple(int(dst.stride(i)) for i in dims) or (1,)
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = tpl_permute(src.data_ptr(), dst.data_ptr(), src.element_size(), ext, ss, ds, (0, 0), 1, sp)
+    if st != TPL_OK:
+        raise TplError(st, tpl_last_error())
+
+
 def permute(dst, src, extents: Sequence[int], src_strides: Sequence[int], dst_strides: Sequence[int],
             src_offset: int = 0, dst_offset: int = 0, batch: int = 1, dtype_bytes: Optional[int] = None,
             stream=None, src_swizzle=None, dst_swizzle=None) -> None:

@@ -630,3 +630,17 @@ def test_bench_buffers_cover_every_layout():
     # the undersized dense guess would not hold the gapped destination
     wl = cases[-3]
     assert bench.buffer_bytes(wl)[1] > wl.elements * wl.w
+
+
+def test_copy_view_checks_its_arguments_on_the_host():
+    import torch
+    x = torch.zeros(4, 8)
+    with pytest.raises(tpl.TplError) as e:
+        tpl.copy_view(torch.zeros(8, 4), x)
+    assert e.value.status == tpl.TPL_E_EXTENT
+    with pytest.raises(tpl.TplError) as e:
+        tpl.copy_view(torch.zeros(4, 8, dtype=torch.float16), x)
+    assert e.value.status == tpl.TPL_E_DTYPE
+    with pytest.raises(tpl.TplError) as e:
+        tpl.copy_view(torch.zeros(4, 8), x)   # host tensors: nothing is launched
+    assert e.value.status == tpl.TPL_E_ARG

@@ -390,3 +390,70 @@ def test_big_in_place_transpose_sampled():
     assert torch.equal(buf.view(65536, 65536), x0.view(65536, 65536).t())
     del buf, x0
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# tpl.copy_view: layouts taken from torch views
+
+
+def _storage_bytes(t):
+    import torch
+    return t.contiguous().view(torch.uint8).reshape(-1).cpu().numpy().copy()
+
+
+def _view_case(name, dst_base, dst, src_base, src):
+    torch = _torch()
+    print(f"\n[case] copy_view {name}: shape={tuple(src.shape)} src strides={src.stride()} "
+          f"dst strides={dst.stride()}", flush=True)
+    w = src.element_size()
+    dims = [i for i, e in enumerate(src.shape) if e != 1]
+    ext = tuple(src.shape[i] for i in dims)
+    ss = tuple(src.stride(i) for i in dims)
+    ds = tuple(dst.stride(i) for i in dims)
+    same = src_base.data_ptr() == dst_base.data_ptr()
+    xs = _storage_bytes(src_base)
+    ref = xs.copy() if same else _storage_bytes(dst_base)
+    oracle.permute(xs, ref, w, ext, ss, ds, (src.storage_offset(), dst.storage_offset()), 1)
+    tpl.copy_view(dst, src)
+    torch.cuda.synchronize()
+    got = _storage_bytes(dst_base)
+    assert np.array_equal(got, ref), f"{name}: {int(np.count_nonzero(got != ref))} bytes differ"
+
+
+def test_copy_view_matches_oracle():
+    torch = _torch()
+    g = torch.Generator("cuda").manual_seed(21)
+
+    def nbytes(shape, dtype):
+        return int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+
+    def rnd(shape, dtype):   # random bit patterns of any dtype
+        return torch.randint(0, 256, (nbytes(shape, dtype),), dtype=torch.uint8, device="cuda",
+                             generator=g).view(dtype).reshape(shape)
+
+    def filled(shape, dtype):   # sentinel bytes
+        return torch.full((nbytes(shape, dtype),), SENTINEL, dtype=torch.uint8, device="cuda").view(dtype).reshape(shape)
+
+    # a permuted source into a contiguous destination (fp32)
+    a = rnd((64, 128, 32), torch.float32)
+    d = filled((32, 64, 128), torch.float32)
+    _view_case("permuted_src", d, d, a, a.permute(2, 0, 1))
+    # contiguous bf16 source into a transposed destination view
+    a = rnd((96, 200), torch.bfloat16)
+    db = filled((200, 96), torch.bfloat16)
+    _view_case("transposed_dst", db, db.t(), a, a)
+    # a column slice of bytes into a transposed destination
+    a = rnd((128, 300), torch.uint8)
+    db = filled((256, 128), torch.uint8)
+    _view_case("sliced_src", db, db.t(), a, a[:, 7:263])
+    # a broadcast (stride-0) fp16 row into a contiguous block
+    a = rnd((1, 64), torch.float16)
+    d = filled((48, 64), torch.float16)
+    _view_case("broadcast_src", d, d, a, a.expand(48, 64))
+    # a strided sub-view of 8-byte elements into a transposed destination
+    a = rnd((40, 3, 17), torch.float64)
+    db = filled((17, 40), torch.float64)
+    _view_case("strided_subview", db, db.t(), a, a[:, 1, :])
+    # a square matrix onto its own transpose: in place
+    a = rnd((512, 512), torch.float32)
+    _view_case("in_place_transpose", a, a, a, a.t())
