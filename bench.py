@@ -145,16 +145,28 @@ def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
     import numpy as np
     import oracle
     y = np.zeros(buffer_bytes(wl)[1], dtype=np.uint8)
-    oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
-                   wl.src_swizzle, wl.dst_swizzle)   # untimed warm-up (first touch of the output)
-    runs, t0 = 0, time.perf_counter()
-    while True:
+    # The calling thread is pinned to one of its cores while the oracle runs.
+    pinned = None
+    try:
+        before = os.sched_getaffinity(0)
+        pinned = min(before)
+        os.sched_setaffinity(0, {pinned})
+    except (AttributeError, OSError):
+        before = None
+    try:
         oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
-                       wl.src_swizzle, wl.dst_swizzle)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds or runs >= max_runs:
-            break
+                       wl.src_swizzle, wl.dst_swizzle)   # untimed warm-up (first touch of the output)
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.permute(x, y, wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+                           wl.src_swizzle, wl.dst_swizzle)
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds or runs >= max_runs:
+                break
+    finally:
+        if before is not None:
+            os.sched_setaffinity(0, before)
     return {
         "value": round(wl.bytes_moved * runs / el / 1e9, 4),
         "unit": "GB/s",
@@ -162,7 +174,7 @@ def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
         "kind": "oracle",
         "sample": f"the full workload ({wl.elements} elements) permuted {runs} times by the "
                   f"single-threaded C oracle in {el:.1f} s",
-        "host": host_info(),
+        "host": dict(host_info(), pinned_core=pinned),
     }, y
 
 
