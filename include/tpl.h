@@ -70,8 +70,10 @@ enum {
     TPL_KERNEL_REG16 = 4,  /* 16-byte elements: 8x8 element blocks, pure lane remap */
     TPL_KERNEL_COPY = 5,   /* both sides contiguous along one mode: vector copy of runs */
     TPL_KERNEL_SWAP = 6,   /* in-place square transpose: mirrored tile pairs swapped through LDS */
-    TPL_KERNEL_REC = 7     /* records of any size to field rows or back: the dense side as one
+    TPL_KERNEL_REC = 7,    /* records of any size to field rows or back: the dense side as one
                               contiguous block through LDS */
+    TPL_KERNEL_ETILE = 8   /* 2-D tiles through LDS one element per access, for layouts whose
+                              bases, row pitches or swizzle granules rule out 16-byte vectors */
 };
 
 /*

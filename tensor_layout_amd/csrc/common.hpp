@@ -144,6 +144,23 @@ struct QuadArgs {
     Swz zs, zd;          // operand swizzles (byte form)
 };
 
+// Element tiles (TB x TA elements of w bytes).  The LDS row pitch is the
+// row plus one element of at least 4 bytes, an odd number of such units,
+// so that the lanes of a column read (neighbouring rows) hit distinct banks.
+struct EtileShape {
+    int w, tb, ta;
+    constexpr TPL_HD int unit() const { return w < 4 ? 4 : w; }
+    constexpr TPL_HD int pitch() const { return ta * w + unit(); }
+};
+
+// One shape per width: TA elements of a source row make 128 or 256 bytes, TB
+// of a destination row 128 to 1024; 16 KiB per tile; TA and TB divide the
+// 256 threads of a workgroup.
+constexpr EtileShape kEtileShapes[5] = {
+    {1, 128, 128}, {2, 128, 64}, {4, 128, 32}, {8, 64, 32}, {16, 64, 16},
+};
+constexpr TPL_HD int etile_index(int w) { return w == 1 ? 0 : w == 2 ? 1 : w == 4 ? 2 : w == 8 ? 3 : 4; }
+
 // In-place pair swaps walk tile pairs in blocks of kSwapG x kSwapG tiles.
 constexpr int kSwapLogG = 3;
 constexpr int kSwapG = 1 << kSwapLogG;

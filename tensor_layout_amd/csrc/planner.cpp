@@ -344,6 +344,12 @@ static LdsChoice choose_lds(const LdsShape& sh) {
     return LdsChoice{};
 }
 
+const EtileShape* etile_shape(int w) {
+    for (const EtileShape& e : kEtileShapes)
+        if (e.w == w) return &e;
+    return nullptr;
+}
+
 // Tile shapes the library instantiates: (w, TB, TA), largest first.
 // Two 16-byte chunks per thread: measured a little faster than four on the
 // large transposes (more waves, each with less data in flight).
@@ -749,6 +755,40 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
                 p.lds_bytes = (int)(tr * F * w);
                 return p;
             }
+        }
+        // Element tiles: a 2-D transpose whose row pitches, bases or swizzle
+        // granules rule out 16-byte vectors still moves through an LDS tile,
+        // one element per access, neighbouring lanes along source rows on the
+        // way in and along destination rows on the way out.
+        const EtileShape* es = etile_shape(w);
+        if (es && sa % w == 0 && da % w == 0 && ma.e >= 8 && mb.e >= 8) {
+            p.kernel = TPL_KERNEL_ETILE;
+            LdsArgs& l = p.lds;
+            l = LdsArgs{};
+            l.e_b = mb.e;
+            l.e_a = ma.e;
+            l.s_b = mb.s;
+            l.d_a = ma.d;
+            l.ntb = (mb.e + es->tb - 1) / es->tb;
+            l.nta = (ma.e + es->ta - 1) / es->ta;
+            int64_t items = 1;
+            for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
+            l.ntiles = items * l.ntb * l.nta;
+            if (l.ntiles >= ((int64_t)1 << 31)) p.big = true;
+            l.div_nta = make_fastdiv((uint32_t)std::min<int64_t>(l.nta, 0x7fffffff));
+            l.div_ntb = make_fastdiv((uint32_t)std::min<int64_t>(l.ntb, 0x7fffffff));
+            set_modes(l.batch, sh, others, no);
+            l.pitch = es->pitch();
+            p.tile_b = es->tb;
+            p.tile_a = es->ta;
+            p.pitch = l.pitch;
+            p.P = 1;
+            p.block = 256;
+            p.grid = l.ntiles;
+            p.lds_bytes = es->tb * es->pitch();
+            // a whole item in one tile is read into LDS before any of it is written
+            p.unit_is_item = l.ntb == 1 && l.nta == 1;
+            return p;
         }
     }
     choose_gather();

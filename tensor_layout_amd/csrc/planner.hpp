@@ -98,6 +98,9 @@ bool inplace_by_unit(const Plan& p);
 
 const LdsShape* swap_shapes(int* n);
 
+// The element-tile shape for width w (nullptr for other widths).
+const EtileShape* etile_shape(int w);
+
 // The pages' method on one warp region (32 lanes, 32 banks).
 Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
                   int64_t batch, const SwzSpec& zs = SwzSpec(), const SwzSpec& zd = SwzSpec());

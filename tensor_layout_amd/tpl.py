@@ -33,7 +33,7 @@ TPL_GEOM_PAGES32 = 1
 TPL_GEOM_GFX950_HALFWAVE = 2
 TPL_GEOM_GFX950_INPLACE = 3
 
-KERNELS = {0: "none", 1: "gather", 2: "quad", 3: "lds", 4: "reg16", 5: "copy", 6: "swap", 7: "rec"}
+KERNELS = {0: "none", 1: "gather", 2: "quad", 3: "lds", 4: "reg16", 5: "copy", 6: "swap", 7: "rec", 8: "etile"}
 MAX_SHARD = 10
 
 EXPORTED = ("tpl_permute", "tpl_plan", "tpl_status_string", "tpl_last_error", "tpl_permute_staged",

@@ -83,6 +83,10 @@ SF_F16 = Workload("sf_transpose_2^20x4x32_f16", 2, (4, 32), (32, 1), (1, 4), bat
 AOS_TO_SOA = Workload("aos_to_soa_2^24x4_f32", 4, (1 << 24, 4), (4, 1), (1, 1 << 24), seed=_seed(7))
 # An array of 2^24 float3 (xyz) records to 3 field arrays.
 AOS3_TO_SOA = Workload("aos_to_soa_2^24x3_f32", 4, (1 << 24, 3), (3, 1), (1, 1 << 24), seed=_seed(7, 1))
+# The 16384^2 bf16 transpose with source rows one element longer than the
+# row: no row but the first starts on a 16-byte boundary.
+BF16_16K_ODD_PITCH = Workload("transpose_16384x16384_bf16_src_pitch_16385", 2, (16384, 16384), (16385, 1),
+                              (1, 16384), seed=_seed(7, 2))
 # The SF transpose into XOR-swizzled destination tiles: the 16-byte chunk
 # index of each 128-element tile (bits 2..3 of the offset) is XORed with bits
 # 5..6; the swizzle period is one tile.
@@ -100,7 +104,8 @@ BF16_16K_INPLACE = Workload("transpose_16384x16384_bf16_inplace", 2, (16384, 163
 COPY_CALIBRATION = Workload("identity_copy_512MiB_u32", 4, (1 << 27,), (1,), (1,), seed=0x5EED0100)
 
 ALL = ([SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)]
-       + [BF16_16K, W16_4K, OUTER_PERM, SF_SWIZZLED, TILE_SWIZZLED, SF_U8, SF_F16, AOS_TO_SOA, AOS3_TO_SOA])
+       + [BF16_16K, W16_4K, OUTER_PERM, SF_SWIZZLED, TILE_SWIZZLED, SF_U8, SF_F16, AOS_TO_SOA, AOS3_TO_SOA,
+          BF16_16K_ODD_PITCH])
 INPLACE = [BF16_16K_INPLACE]
 
 

@@ -155,6 +155,7 @@ EXPECTED_KERNEL = {
     "sf_transpose_2^20x4x32_f16": "quad",
     "aos_to_soa_2^24x4_f32": "quad",
     "aos_to_soa_2^24x3_f32": "rec",
+    "transpose_16384x16384_bf16_src_pitch_16385": "etile",
 }
 
 

@@ -71,7 +71,7 @@ def test_random_permutations_match_oracle():
         kernels[p.kernel] += 1
         run_case(f"fuzz_{t}", w, ext, ss, ds, offs, batch, seed=t, zs=zs, zd=zd)
     print("kernel mix:", dict(kernels), flush=True)
-    assert {"lds", "gather", "copy", "quad"} <= set(kernels)
+    assert {"lds", "gather", "copy", "quad", "etile"} <= set(kernels)
 
 
 def record_case(rng):
@@ -131,7 +131,7 @@ def test_random_inplace_transposes_match_oracle():
         kernels[p.kernel] += 1
         run_inplace(f"inplace_{t}", w, n, pitch, batch, gap, offset, seed=200 + t, expect_kernel=p.kernel)
     print("kernel mix:", dict(kernels), flush=True)
-    assert kernels["swap"] >= 30
+    assert kernels["swap"] >= 25
 
 
 def test_graph_capture_and_replay():

@@ -151,7 +151,7 @@ RAGGED = [
     ("copy_runs_of_8_bytes", 2, (40, 12), (12, 1), (480, 1), "copy"),
     ("copy_runs_of_4_bytes", 1, (3, 50, 4), (200, 4, 1), (4, 12, 1), "copy"),
     ("rec_unaligned_rows_dense_dst", 2, (130, 1000), (1000, 1), (1, 130), "rec"),
-    ("gather_unaligned_rows_padded_dst", 2, (130, 1000), (1000, 1), (1, 131), "gather"),
+    ("etile_unaligned_rows_padded_dst", 2, (130, 1000), (1000, 1), (1, 131), "etile"),
     ("gather_no_unit_stride", 4, (16, 24), (48, 2), (24, 1), "gather"),
     ("gather_small_modes", 8, (3, 5, 7), (35, 7, 1), (1, 3, 15), "gather"),
     ("lds_broadcast_src", 4, (64, 32), (0, 1), (1, 64), "lds"),
@@ -457,3 +457,50 @@ def test_copy_view_matches_oracle():
     # a square matrix onto its own transpose: in place
     a = rnd((512, 512), torch.float32)
     _view_case("in_place_transpose", a, a, a, a.t())
+
+
+# ---------------------------------------------------------------------------
+# Element tiles: 2-D transposes that 16-byte vectors cannot serve (odd row
+# pitches, element offsets, small swizzle granules), tiled through LDS one
+# element per access.
+
+ETILE = [
+    # name, w, extents, src strides, dst strides, element offsets, batch, src swizzle, dst swizzle
+    ("u8_odd_pitches", 1, (300, 260), (261, 1), (1, 301), (0, 0), 1, None, None),
+    ("bf16_odd_pitches_ragged", 2, (257, 513), (515, 1), (1, 257), (0, 0), 1, None, None),
+    ("f32_offsets_batch", 4, (200, 300), (301, 1), (1, 200), (3, 1), 3, None, None),
+    ("f64_odd_pitches", 8, (100, 90), (91, 1), (1, 101), (0, 0), 1, None, None),
+    ("u16_src_offset_odd", 2, (128, 256), (256, 1), (1, 128), (1, 0), 2, None, None),
+    ("f32_into_8B_granule_swizzle", 4, (64, 96), (96, 1), (1, 64), (0, 0), 2, None, (3, 1, 3)),
+    ("u8_from_2B_granule_swizzle", 1, (96, 160), (160, 1), (1, 96), (0, 0), 1, (2, 1, 4), None),
+    ("below_one_tile", 4, (12, 20), (21, 1), (1, 13), (0, 0), 5, None, None),
+]
+
+
+@pytest.mark.parametrize("case", ETILE, ids=lambda c: c[0])
+def test_element_tiles_match_oracle(case):
+    name, w, ext, ss, ds, offs, batch, zs, zd = case
+    run_case(f"etile_{name}", w, ext, ss, ds, offs, batch, seed=zlib.crc32(name.encode()) & 0xFFFF,
+             expect_kernel="etile", zs=zs, zd=zd)
+
+
+def test_element_tiles_full_size_sampled():
+    """A 16384 x 16384 bf16 transpose with source rows 16385 elements apart
+    (no 16-byte alignment on any row but the first): sampled coordinates
+    against the oracle's address rule and the whole result against strided
+    views."""
+    torch = _torch()
+    ext, ss, ds = (16384, 16384), (16385, 1), (1, 16384)
+    plan = tpl.tpl_plan(2, ext, ss, ds)
+    assert plan.kernel == "etile", plan
+    si, di, span_s, span_d = sampled_pairs(ext, ss, ds, 1, 17)
+    print("\n[case] element tiles 16384^2 bf16, source pitch 16385", flush=True)
+    gen = torch.Generator("cuda").manual_seed(9)
+    x = torch.randint(0, 256, (span_s * 2,), dtype=torch.uint8, device="cuda", generator=gen).view(torch.int16)
+    d = torch.full((span_d * 2,), SENTINEL, dtype=torch.uint8, device="cuda").view(torch.int16)
+    tpl.permute(d, x, ext, ss, ds, dtype_bytes=2)
+    torch.cuda.synchronize()
+    xs = x[torch.tensor(si, device="cuda")].cpu().numpy()
+    ys = d[torch.tensor(di, device="cuda")].cpu().numpy()
+    assert np.array_equal(xs, ys)
+    assert torch.equal(torch.as_strided(x, ext, ss), torch.as_strided(d, ext, ds))
