@@ -439,7 +439,7 @@ def main():
     ap.add_argument("--xor-k", type=int, default=-1, help="staged entry: force this XOR k (-1 = planner's)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 
