@@ -37,11 +37,35 @@ KERNEL_SOURCES = [os.path.join(ROOT, "tensor_layout_amd", "csrc", f)
                   for f in ("kernels.hip", "common.hpp", "planner.cpp", "planner.hpp")]
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments and blank space removed, so that edits of
+    comments alone keep the counters that were taken on the same code."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

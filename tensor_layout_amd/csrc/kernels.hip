@@ -227,7 +227,7 @@ __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
 // LDS kernel: one workgroup moves a TB x TA tile (TB along the destination-
 // contiguous mode b, TA along the source-contiguous mode a).
 //
-// Phase 1: every thread loads four 16-byte chunks of source rows and writes
+// Phase 1: every thread loads CPT (two) 16-byte chunks of source rows and writes
 // them to LDS (row pitch chosen by the planner) in 16/WW pieces, the piece
 // order XOR-rotated per lane: piece = r ^ ((lane >> shift_w) & mask_w).
 // Barrier.  Phase 2: every thread gathers, for one column of the tile and

@@ -645,3 +645,14 @@ def test_copy_view_checks_its_arguments_on_the_host():
     with pytest.raises(tpl.TplError) as e:
         tpl.copy_view(torch.zeros(4, 8), x)   # host tensors: nothing is launched
     assert e.value.status == tpl.TPL_E_ARG
+
+
+def test_counter_hash_ignores_comments_only():
+    """The profiles' source hash: comments and spacing do not count, code does."""
+    import bench
+    a = 'int f(int x) { return x + 1; }  // add one\n/* "quoted" */ const char* s = "a // b";\n'
+    b = '// a comment\nint f(int x)\n{\n    return x + 1;   /* add one */\n}\nconst char* s = "a // b";\n'
+    c = 'int f(int x) { return x + 2; }\nconst char* s = "a // b";\n'
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+    assert '"a // b"' in bench._code_only(a)
