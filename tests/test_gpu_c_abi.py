@@ -46,6 +46,11 @@ def run_client(tmp_path, name, w, ext, ss, ds, offs=(0, 0), batch=1):
     ("bf16_1000x700_offsets", 2, (1000, 700), (700, 1), (1, 1000), (8, 24), 1),
     ("u8_axes0231", 1, (4, 128, 32, 32), (131072, 1024, 32, 1), (131072, 1, 4096, 128), (0, 0), 1),
     ("u128_300x200", 16, (300, 200), (200, 1), (1, 300), (0, 0), 1),
+    ("rec_float3_aos_to_soa", 4, (3000, 3), (3, 1), (1, 3000), (0, 0), 1),
+    ("etile_bf16_odd_pitch", 2, (300, 500), (501, 1), (1, 300), (0, 0), 1),
+    ("copy_row_blocks_f32", 4, (8, 16, 256), (4096, 256, 1), (256, 2048, 1), (0, 0), 1),
+    ("quad_u8_sf", 1, (4, 32), (32, 1), (1, 4), (0, 0), 2048),
+    ("gather_no_unit_stride", 4, (16, 24), (48, 2), (24, 1), (0, 0), 1),
 ], ids=lambda c: c[0])
 def test_c_client_matches_oracle(tmp_path, case):
     name, w, ext, ss, ds, offs, batch = case
