@@ -504,3 +504,30 @@ def test_element_tiles_full_size_sampled():
     ys = d[torch.tensor(di, device="cuda")].cpu().numpy()
     assert np.array_equal(xs, ys)
     assert torch.equal(torch.as_strided(x, ext, ss), torch.as_strided(d, ext, ds))
+
+
+# ---------------------------------------------------------------------------
+# The largest rank the ABI takes: 8 modes, permuted axis orders.
+
+def _row_major_order(ext, order):
+    st = [0] * len(ext)
+    acc = 1
+    for ax in reversed(order):
+        st[ax] = acc
+        acc *= ext[ax]
+    return tuple(st)
+
+
+RANK8 = [
+    ("rank8_u32_scrambled", 4, (2, 3, 2, 4, 2, 3, 2, 5), (7, 0, 5, 2, 3, 6, 1, 4), 1),
+    ("rank8_u16_last_axis_kept", 2, (2, 2, 3, 2, 2, 3, 4, 64), (1, 0, 3, 2, 5, 4, 6, 7), 3),
+    ("rank8_u8_reversed", 1, (3, 2, 2, 3, 2, 2, 5, 32), (7, 6, 5, 4, 3, 2, 1, 0), 2),
+]
+
+
+@pytest.mark.parametrize("case", RANK8, ids=lambda c: c[0])
+def test_rank8_permutations_match_oracle(case):
+    name, w, ext, order, batch = case
+    ss = _row_major_order(ext, list(range(8)))
+    ds = _row_major_order(ext, list(order))
+    run_case(name, w, ext, ss, ds, (0, 0), batch, seed=zlib.crc32(name.encode()) & 0xFFFF)
