@@ -33,8 +33,11 @@ METRIC = "permute_layout GB/s (rd+wr) & % of HBM peak, batched 4x32 fp32 SF tran
 PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 2 << 30      # src+dst bytes cycled through per rotation
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "tensor_layout_amd", "csrc", f)
-                  for f in ("kernels.hip", "common.hpp", "planner.cpp", "planner.hpp")]
+# The sources of the profiled kernels and their planner (not the staged
+# entry or the bank probe, which the counters do not cover).
+_CSRC = os.path.join(ROOT, "tensor_layout_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(_CSRC, f) for f in os.listdir(_CSRC)
+                        if f.endswith((".hip", ".hpp", ".cpp")) and f not in ("staged.hip", "lds_probe.hip"))
 
 
 def _code_only(text: str) -> str:

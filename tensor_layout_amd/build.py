@@ -2,15 +2,21 @@
 
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtpl.so")
-SOURCES = ["planner.cpp", "kernels.hip", "staged.hip"]
+# One translation unit per kernel family, compiled in parallel.
+SOURCES = ["planner.cpp", "kernels.hip", "kernels_stream.hip", "kernels_quad.hip", "kernels_lds.hip",
+           "kernels_lds_w12.hip", "kernels_lds_w48.hip", "kernels_lds_w16.hip",
+           "kernels_swap.hip", "kernels_rec.hip", "kernels_etile.hip", "staged.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -45,13 +51,27 @@ CLIENT = os.path.join(ROOT, "tests", "c_abi", "abi_client")
 
 
 def build(verbose: bool = False) -> str:
-    """Build libtpl.so, the LDS bank-geometry probe and the C ABI test client (all in-tree)."""
-    tmp = LIB + ".tmp"
-    _run([HIPCC] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    ptmp = PROBE + ".tmp"
-    _run([HIPCC] + PROBE_FLAGS + [os.path.join(CSRC, "lds_probe.hip"), "-o", ptmp], verbose)
-    os.replace(ptmp, PROBE)
+    """Build libtpl.so, the LDS bank-geometry probe and the C ABI test client (all in-tree).
+
+    Every source is compiled to an object on its own (in parallel, with the
+    probe alongside), then the objects are linked."""
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objdir = tempfile.mkdtemp(prefix="tpl_build_")
+    try:
+        objs = [os.path.join(objdir, s + ".o") for s in SOURCES]
+        ptmp = PROBE + ".tmp"
+        jobs = [[HIPCC] + compile_flags + ["-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+        jobs.append([HIPCC] + PROBE_FLAGS + [os.path.join(CSRC, "lds_probe.hip"), "-o", ptmp])
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            for f in [ex.submit(_run, j, verbose) for j in jobs]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+        os.replace(tmp, LIB)
+        os.replace(ptmp, PROBE)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     if os.path.exists(CLIENT_SRC):
         ctmp = CLIENT + ".tmp"
         _run([HIPCC, "-O2", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"), CLIENT_SRC,

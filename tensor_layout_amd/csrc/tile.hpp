@@ -1,0 +1,146 @@
+// tile.hpp -- the two phases of an LDS tile (global rows into LDS with
+// XOR-ordered pieces; LDS columns out to global rows with XOR-ordered rows),
+// shared by the tiled transpose and the in-place pair swap.
+#pragma once
+
+#include "device.hpp"
+
+namespace tpl {
+
+template <int N>
+__device__ __forceinline__ void unrotate(uint32_t (&d)[N], int key) {
+    // d[r] holds row r ^ key; afterwards d[m] holds row m.
+#pragma unroll
+    for (int bi = 0; (1 << bi) < N; ++bi) {
+        const bool sw = (key >> bi) & 1;
+#pragma unroll
+        for (int x = 0; x < N; ++x) {
+            if (x & (1 << bi)) continue;
+            uint32_t p0 = d[x], p1 = d[x | (1 << bi)];
+            d[x] = sw ? p1 : p0;
+            d[x | (1 << bi)] = sw ? p0 : p1;
+        }
+    }
+}
+
+// Phase 1 of an LDS tile: the TB x TA source tile at st (rows srow bytes
+// apart) through registers into LDS, element (b, a) at b * pitch + a * W.
+// Each thread loads CPT 16-byte chunks, then writes them in 16 / WW pieces
+// whose order is rotated by key_w.
+template <int W, int TB, int TA, int CPT, int WW, bool SWZ = false>
+__device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* gsrc, int64_t pt, int64_t srow, int pitch,
+                                            int t, int key_w, const Swz& z = Swz{}) {
+    constexpr LdsShape SH{W, TB, TA, CPT};
+    constexpr int NT = SH.threads();
+    constexpr int CPR = TA * W / 16;
+    constexpr int NP = 16 / WW;   // pieces per chunk
+    u32x4 v[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int cid = t + k * NT;
+        v[k] = ld16(at<SWZ>(gsrc, pt + (cid / CPR) * srow + (cid % CPR) * 16, z));
+    }
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const int cid = t + k * NT;
+        uint8_t* row = lds + (cid / CPR) * pitch + (cid % CPR) * 16;
+        if constexpr (NP == 1) {
+            *reinterpret_cast<u32x4*>(row) = v[k];
+        } else if constexpr (NP == 2) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int h = r ^ key_w;
+                u32x2 p = h ? u32x2{v[k].z, v[k].w} : u32x2{v[k].x, v[k].y};
+                *reinterpret_cast<u32x2*>(row + h * 8) = p;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int h = r ^ key_w;
+                uint32_t p = h == 0 ? v[k].x : h == 1 ? v[k].y : h == 2 ? v[k].z : v[k].w;
+                *reinterpret_cast<uint32_t*>(row + h * 4) = p;
+            }
+        }
+    }
+}
+
+// Phase 2 of an LDS tile: LDS through registers to the destination tile at
+// dt (destination rows d_a elements apart).  A thread reads R words of one
+// LDS column, rows in the order r ^ key_r, restores their order, packs them
+// and stores 16-byte destination chunks.
+template <int W, int TB, int TA, int CPT, bool SWZ = false>
+__device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* gdst, int64_t pt, int64_t d_a, int pitch,
+                                              int t, int key_r, const Swz& z = Swz{}) {
+    constexpr LdsShape SH{W, TB, TA, CPT};
+    constexpr int NT = SH.threads();
+    constexpr int R = SH.reads_per_group();       // reads per group
+    constexpr int GPT = SH.groups_per_thread();   // groups per thread
+#pragma unroll
+    for (int k2 = 0; k2 < GPT; ++k2) {
+        if (SH.groups() % NT != 0 && t + k2 * NT >= SH.groups()) break;
+        int col, q;
+        lds_group(SH, t, k2, &col, &q);
+        const uint8_t* base = lds + (q * R) * pitch + col * SH.read_bytes();
+        if constexpr (W == 16) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(base);
+            st16(at<SWZ>(gdst, pt + (int64_t)col * d_a * 16 + q * 16, z), x);
+        } else if constexpr (W == 8) {
+            uint32_t lo[2], hi[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int j = r ^ key_r;
+                u32x2 x = *reinterpret_cast<const u32x2*>(base + j * pitch);
+                lo[r] = x.x;
+                hi[r] = x.y;
+            }
+            unrotate<2>(lo, key_r);
+            unrotate<2>(hi, key_r);
+            st16(at<SWZ>(gdst, pt + (int64_t)col * d_a * W + q * 16, z), u32x4{lo[0], hi[0], lo[1], hi[1]});
+        } else {
+            uint32_t d[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int j = r ^ key_r;
+                d[r] = *reinterpret_cast<const uint32_t*>(base + j * pitch);
+            }
+            unrotate<R>(d, key_r);
+            if constexpr (W == 4) {
+                st16(at<SWZ>(gdst, pt + (int64_t)col * d_a * 4 + q * 16, z), u32x4{d[0], d[1], d[2], d[3]});
+            } else if constexpr (W == 2) {
+                // d[m] = (b0+m, a=2col) | (b0+m, a=2col+1) << 16
+                u32x4 o0, o1;
+                uint32_t* p0 = reinterpret_cast<uint32_t*>(&o0);
+                uint32_t* p1 = reinterpret_cast<uint32_t*>(&o1);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const uint32_t x = d[2 * kk], y = d[2 * kk + 1];
+                    p0[kk] = (x & 0xffffu) | (y << 16);
+                    p1[kk] = (x >> 16) | (y & 0xffff0000u);
+                }
+                const int64_t out = pt + (int64_t)(2 * col) * d_a * 2 + q * 16;
+                st16(at<SWZ>(gdst, out, z), o0);
+                st16(at<SWZ>(gdst, out + d_a * 2, z), o1);
+            } else {
+                // W == 1: d[m] holds bytes (b0+m, a=4col+t), t = 0..3.
+                u32x4 o[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    uint32_t* p = reinterpret_cast<uint32_t*>(&o[tt]);
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int sh = 8 * tt;
+                        p[kk] = ((d[4 * kk] >> sh) & 0xffu) | (((d[4 * kk + 1] >> sh) & 0xffu) << 8) |
+                                (((d[4 * kk + 2] >> sh) & 0xffu) << 16) | (((d[4 * kk + 3] >> sh) & 0xffu) << 24);
+                    }
+                }
+                const int64_t out = pt + (int64_t)(4 * col) * d_a + q * 16;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) st16(at<SWZ>(gdst, out + tt * d_a, z), o[tt]);
+            }
+        }
+    }
+}
+
+// One element of W bytes, moved in pieces of min(W, 4) bytes (the LDS pitch
+// and the element bases are multiples of that).
+}  // namespace tpl
