@@ -1,11 +1,16 @@
 """Thin ctypes binding of libtpl.so (argument marshalling only).
 
-The names follow the C ABI in include/tpl.h: ``tpl_permute``, ``tpl_plan``,
-``tpl_status_string`` and ``tpl_last_error``.  ``permute`` is a convenience
-wrapper over torch tensors: it checks dtypes, extents and byte ranges, then
-calls ``tpl_permute`` on the tensors' device pointers and torch's current
-stream.  Every step of the permutation runs in the library's HIP kernels; if
-the library is missing or cannot be loaded every call raises.
+The names follow the C ABI in include/tpl.h: ``tpl_permute``,
+``tpl_permute_swizzled``, ``tpl_permute_staged``, ``tpl_plan`` (with the
+swizzled form behind its keyword arguments), ``tpl_status_string`` and
+``tpl_last_error``.  ``PreparedPermute`` marshals one layout once for
+repeated calls.  Two conveniences take torch tensors: ``permute`` (flat
+storage plus explicit extents and strides; it checks dtypes, extents and
+byte ranges) and ``copy_view`` (both layouts read off two views of one
+shape); both call ``tpl_permute`` on the tensors' device pointers and
+torch's current stream.  Every step of the permutation runs in the
+library's HIP kernels; if the library is missing or cannot be loaded every
+call raises.
 """
 
 from __future__ import annotations
