@@ -531,3 +531,35 @@ def test_rank8_permutations_match_oracle(case):
     ss = _row_major_order(ext, list(range(8)))
     ds = _row_major_order(ext, list(order))
     run_case(name, w, ext, ss, ds, (0, 0), batch, seed=zlib.crc32(name.encode()) & 0xFFFF)
+
+
+# ---------------------------------------------------------------------------
+# Every tile shape the tiled transpose instantiates, picked by extents just
+# past the shape (ragged edges on both modes), as one item and as two items
+# of a batch mode.
+
+LDS_SHAPES = [(1, 128, 128), (1, 64, 128), (2, 256, 64), (2, 128, 64), (2, 32, 64), (4, 64, 64), (4, 32, 32),
+              (8, 32, 64), (8, 16, 32), (16, 64, 16), (16, 16, 64), (16, 16, 16)]
+
+
+def _shape_case(w, tb, ta):
+    eb, ea = tb + 3, ta + 5
+    pa = -(-ea * w // 16) * 16 // w    # rows padded to whole 16-byte chunks
+    pb = -(-eb * w // 16) * 16 // w
+    return eb, ea, pa, pb
+
+
+@pytest.mark.parametrize("shape", LDS_SHAPES, ids=lambda s: f"w{s[0]}_{s[1]}x{s[2]}")
+def test_every_lds_tile_shape(shape):
+    w, tb, ta = shape
+    eb, ea, pa, pb = _shape_case(w, tb, ta)
+    ext, ss, ds = (eb, ea), (pa, 1), (1, pb)
+    p = tpl.tpl_plan(w, ext, ss, ds)
+    assert p.kernel == "lds" and tuple(p.tile) == (tb, ta), p
+    run_case(f"lds_shape_w{w}_{tb}x{ta}", w, ext, ss, ds, seed=tb * 7 + ta)
+    # two items 16-byte aligned apart: one batch mode
+    item_s, item_d = eb * pa + 16 // min(w, 16), ea * pb + 16 // min(w, 16)
+    ext3, ss3, ds3 = (2, eb, ea), (item_s, pa, 1), (item_d, 1, pb)
+    p3 = tpl.tpl_plan(w, ext3, ss3, ds3)
+    assert p3.kernel == "lds" and tuple(p3.tile) == (tb, ta), p3
+    run_case(f"lds_shape_w{w}_{tb}x{ta}_two_items", w, ext3, ss3, ds3, seed=tb * 7 + ta + 1)
