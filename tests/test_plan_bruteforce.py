@@ -251,3 +251,35 @@ def test_bruteforce_agrees_with_the_library_halfwave_plan(w):
             assert (p.P, p.k, p.shift, p.mask) == want, (w, ext, ss, ds, p, want)
             found += 1
     assert found > 0
+
+
+# The exhaustive 4-mode family: every shape of 4 modes with extents in
+# {1, 2, 4, 8, 16, 32} and 32 to 256 elements (extent-1 modes included, so
+# the oracle must drop them), row-major source, destination row-major in
+# every one of the 24 axis orders.
+
+def family4():
+    import math
+    vals = (1, 2, 4, 8, 16, 32)
+    for ext in itertools.product(vals, repeat=4):
+        if 32 <= math.prod(ext) <= 256:
+            for order in itertools.permutations(range(4)):
+                yield ext, row_major(ext, [0, 1, 2, 3], 0), row_major(ext, list(order), 0)
+
+
+CASES4 = list(family4())
+
+
+# Every layout at the 4-byte width; a third of them, a different third at each
+# other width, so that every layout is also checked at a second width and the
+# CPU suite stays short.
+@pytest.mark.parametrize("w,start,step", [(4, 0, 1), (1, 0, 3), (2, 1, 3), (8, 2, 3), (16, 0, 3)])
+def test_bruteforce_agrees_on_every_4_mode_layout(w, start, step):
+    assert len(CASES4) == 8760
+    for ext, ss, ds in CASES4[start::step]:
+        want = brute_plan(w, ext, ss, ds)
+        p = po.plan(w, ext, ss, ds)
+        got = None if not p.ok else (p.P, p.k, p.shift, p.mask)
+        assert got == want, (w, ext, ss, ds, p, want)
+        if want is None:
+            assert p.reason == po.REASON_NO_K
