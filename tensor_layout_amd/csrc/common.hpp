@@ -144,20 +144,43 @@ struct QuadArgs {
     Swz zs, zd;          // operand swizzles (byte form)
 };
 
-// Element tiles (TB x TA elements of w bytes).  The LDS row pitch is the
-// row plus one element of at least 4 bytes, an odd number of such units,
-// so that the lanes of a column read (neighbouring rows) hit distinct banks.
+// Element tiles (TB x TA elements of w bytes), in two forms.
+//
+// Element form (swizzled operands): one element per access; the LDS row
+// pitch is the row plus one element of at least 4 bytes, an odd number of
+// such units, so that the lanes of a column read (neighbouring rows) hit
+// distinct banks.
+//
+// Vector form (plain operands, w <= 4): each source row piece is read as the
+// 16-byte aligned chunks that cover it, at most TA w / 16 + 1, and kept in
+// LDS as read: row bb starts at vrow(bb) = bb rp + sk (bb >> le), and its
+// element aa sits lead(bb) + aa w bytes further, lead(bb) being the row
+// piece's address mod 16.  Destination row pieces are written as aligned
+// 16-byte chunks, element by element only in a chunk the piece covers in
+// part.  rp, sk and le are chosen on the measured gfx950 bank geometry so
+// that neither the chunk writes (pieces of g bytes: b128, b64 pairs or b32)
+// nor the element reads of a destination chunk (16 / w rows of one column
+// per lane) meet a bank conflict.
 struct EtileShape {
     int w, tb, ta;
+    int rp, sk, le, g;   // vector form: LDS row pitch, skew bytes per 2^le rows, write piece
     constexpr TPL_HD int unit() const { return w < 4 ? 4 : w; }
     constexpr TPL_HD int pitch() const { return ta * w + unit(); }
+    constexpr TPL_HD int vrow(int bb) const { return bb * rp + sk * (bb >> le); }
+    constexpr TPL_HD int vbytes() const { return vrow(tb); }
 };
 
 // One shape per width: TA elements of a source row make 128 or 256 bytes, TB
 // of a destination row 128 to 1024; 16 KiB per tile; TA and TB divide the
-// 256 threads of a workgroup.
+// 256 threads of a workgroup.  8- and 16-byte elements take the element
+// form only (an 8-byte element per lane measured as fast as or faster than
+// 16-byte chunks with their realignment).
 constexpr EtileShape kEtileShapes[5] = {
-    {1, 128, 128}, {2, 128, 64}, {4, 128, 32}, {8, 64, 32}, {16, 64, 16},
+    {1, 128, 128, 144, 16, 4, 16},
+    {2, 128, 64, 152, 8, 3, 8},
+    {4, 128, 32, 148, 4, 2, 4},
+    {8, 64, 32, 0, 0, 0, 0},
+    {16, 64, 16, 0, 0, 0, 0},
 };
 constexpr TPL_HD int etile_index(int w) { return w == 1 ? 0 : w == 2 ? 1 : w == 4 ? 2 : w == 8 ? 3 : 4; }
 
@@ -184,6 +207,9 @@ struct LdsArgs {
     int64_t nbl;
     FastDiv div_nbl;
     int32_t scalar;
+    // Element tiles only: 1 for the vector form (16-byte chunks kept in LDS
+    // as read), 0 for the element form.
+    int32_t vform;
     Swz zs, zd;          // operand swizzles (byte form)
 };
 

@@ -1,20 +1,24 @@
-// kernels_etile.hip -- 2-D transposes through LDS one element per access.
+// kernels_etile.hip -- 2-D transposes through LDS whose rows are not aligned
+// to 16 bytes (or whose swizzle granules are shorter than 16 bytes).
 #include "device.hpp"
 
 namespace tpl {
 
 // ---------------------------------------------------------------------------
 // Element tiles: a TB x TA tile (TB along the destination-contiguous mode b,
-// TA along the source-contiguous mode a) staged through LDS one element per
-// access, for 2-D transposes whose row pitches, bases or swizzle granules
-// rule out the 16-byte vectors of k_lds.  Loading, neighbouring lanes walk
-// a source row (TA elements: 128 or 256 bytes); storing, they walk a
-// destination row.  TA and TB divide the 256 threads, so each thread keeps
-// one column on each side and steps by whole rows: its addresses advance by
-// a constant.  The LDS pitch is the row plus one unit of max(w, 4) bytes, an
-// odd number of units, so the column read of phase 2 (lanes on neighbouring
-// rows) meets no bank conflict; the row write of phase 1 is contiguous.
-// Tiles follow the k_lds order.
+// TA along the source-contiguous mode a) staged through LDS, for 2-D
+// transposes whose row pitches, bases or swizzle granules rule out the
+// 16-byte vectors of k_lds.  Plain operands take the vector form
+// (etile_vec_loop): 16-byte aligned chunks in and out, the rows' offsets
+// from 16 bytes absorbed in the LDS addresses.  Swizzled operands take the
+// element form (etile_loop): one element per access; loading, neighbouring
+// lanes walk a source row (TA elements: 128 or 256 bytes); storing, they
+// walk a destination row.  TA and TB divide the 256 threads, so each thread
+// keeps one column on each side and steps by whole rows: its addresses
+// advance by a constant.  The LDS pitch is the row plus one unit of
+// max(w, 4) bytes, an odd number of units, so the column read of phase 2
+// (lanes on neighbouring rows) meets no bank conflict; the row write of
+// phase 1 is contiguous.  Tiles follow the k_lds order in both forms.
 
 template <int W> struct Elem;
 template <> struct Elem<1> { typedef uint8_t type; };
@@ -69,6 +73,139 @@ __device__ __forceinline__ void etile_loop(const LdsArgs& a, uint8_t* lds) {
     }
 }
 
+// Vector form (plain operands, W <= 4).  Loading, thread t takes chunk
+// t % QS of rows t / QS + i RS, then thread t < TB the one extra chunk of row
+// t that a row piece not starting on 16 bytes reaches into.  A chunk may hold
+// bytes outside the layout; they share its aligned 16 bytes, hence its page,
+// with bytes of the layout, and are never stored.  Storing, thread t takes
+// chunk t % QD of the destination rows (tile columns) t / QD + i CS, then
+// thread t < TA the extra chunk of column t; 16 neighbouring lanes (8 for
+// bytes, 32 for 4-byte elements) cover a column's row piece.
+template <int W, int NB, bool BIG>
+__device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
+    typedef typename Elem<W>::type T;
+    constexpr EtileShape ES = kEtileShapes[etile_index(W)];
+    constexpr int TB = ES.tb, TA = ES.ta, NT = 256, E = 16 / W;
+    constexpr int QS = TA * W / 16, QD = TB * W / 16;   // chunks of a whole source / destination row piece
+    constexpr int RS = NT / QS, CS = NT / QD;           // rows / columns per step
+    constexpr int NS = TB / RS, ND = TA / CS;           // steps
+    static_assert(NT % QS == 0 && NT % QD == 0 && TB % RS == 0 && TA % CS == 0 && TB <= NT && TA <= NT,
+                  "tile must tile the threads");
+    static_assert(ES.rp >= (QS + 1) * 16 && ES.vrow(1) % ES.g == 0 && ES.rp % ES.g == 0 && ES.sk % ES.g == 0,
+                  "LDS rows must hold every chunk at the write piece's alignment");
+    const int t = threadIdx.x;
+    const int q1 = t % QS, r1 = t / QS;
+    const int q2 = t % QD, c2 = t / QD;
+    const uint32_t pm = (uint32_t)(a.s_b * W) & 15;   // lead change per source row
+    for (int64_t tile = blockIdx.x; tile < a.ntiles; tile += gridDim.x) {
+        int64_t rest, tq, item, tbi, tai, wrap;
+        split<BIG>(tile, a.ntb, a.div_ntb, rest, tbi);
+        split<BIG>(rest, a.nta, a.div_nta, item, tq);
+        split<BIG>(tq + tbi, a.nta, a.div_nta, wrap, tai);
+        int64_t so, d_o;
+        modes_offsets<NB, BIG>(a.batch, item, so, d_o);
+        const int64_t b0 = tbi * TB, a0 = tai * TA;
+        const int nb = (int)(a.e_b - b0 < TB ? a.e_b - b0 : TB), na = (int)(a.e_a - a0 < TA ? a.e_a - a0 : TA);
+        const uint8_t* s0 = a.src + (so + b0 * a.s_b + a0) * W;   // row 0 of the tile's source piece
+        const uint32_t L0 = (uint32_t)(uintptr_t)s0 & 15;
+        const int64_t srow = a.s_b * W;
+        {
+            u32x4 v[NS + 1];
+            int at_lds[NS + 1];
+            bool on[NS + 1];
+#pragma unroll
+            for (int i = 0; i <= NS; ++i) {
+                const int bb = i < NS ? r1 + i * RS : t;
+                const int q = i < NS ? q1 : QS;
+                const int lead = (int)((L0 + (uint32_t)bb * pm) & 15);
+                on[i] = (i < NS || t < TB) && bb < nb && q * 16 < lead + na * W;
+                at_lds[i] = ES.vrow(bb) + q * 16;
+                if (on[i]) {
+                    // The first and last chunk of a row piece may hold bytes
+                    // of the neighbouring tiles' pieces: ordinary loads keep
+                    // them in L2 for those tiles (non-temporal ones let the
+                    // 16384^2 bf16 transpose with pitch 16385 fetch 1.8x).
+                    const uint8_t* g = s0 + bb * srow - lead + q * 16;
+                    if (q == 0 || q * 16 + 16 > lead + na * W) v[i] = *reinterpret_cast<const u32x4*>(g);
+                    else v[i] = ld16(g);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i <= NS; ++i) {
+                if (!on[i]) continue;
+                uint8_t* l = lds + at_lds[i];
+                if constexpr (ES.g == 16) {
+                    *reinterpret_cast<u32x4*>(l) = v[i];
+                } else if constexpr (ES.g == 8) {
+                    // Lanes 8 chunks apart write their halves in opposite order.
+                    const int q = i < NS ? q1 : QS;
+                    const u32x2 lo = {v[i].x, v[i].y}, hi = {v[i].z, v[i].w};
+                    const bool h = (q >> 3) & 1;
+                    *reinterpret_cast<u32x2*>(l + (h ? 8 : 0)) = h ? hi : lo;
+                    *reinterpret_cast<u32x2*>(l + (h ? 0 : 8)) = h ? lo : hi;
+                } else {
+                    uint32_t* d = reinterpret_cast<uint32_t*>(l);
+                    d[0] = v[i].x;
+                    d[1] = v[i].y;
+                    d[2] = v[i].z;
+                    d[3] = v[i].w;
+                }
+            }
+        }
+        __syncthreads();
+        {
+            uint8_t* d0 = a.dst + (d_o + a0 * a.d_a + b0) * W;   // the tile's destination row 0
+            const int64_t drow = a.d_a * W;
+#pragma unroll
+            for (int i = 0; i <= ND; ++i) {
+                const int aa = i < ND ? c2 + i * CS : t;
+                const int q = i < ND ? q2 : QD;
+                if (!((i < ND || t < TA) && aa < na)) continue;
+                uint8_t* D = d0 + aa * drow;
+                const int lead = (int)((uint32_t)(uintptr_t)D & 15);
+                const int rel = q * 16 - lead;   // chunk start, bytes from the row piece's start
+                if (rel >= nb * W) continue;
+                const int bbf = rel / W;         // exact: lead is a multiple of W
+                union {
+                    u32x4 v;
+                    T e[E];
+                } u;
+#pragma unroll
+                for (int j = 0; j < E; ++j) {
+                    // rows outside the piece read row 0 (a partial chunk stores no such element)
+                    const int bb = (unsigned)(bbf + j) < (unsigned)nb ? bbf + j : 0;
+                    const int ls = (int)((L0 + (uint32_t)bb * pm) & 15);
+                    u.e[j] = *reinterpret_cast<const T*>(lds + ES.vrow(bb) + ls + aa * W);
+                }
+                if (rel >= 0 && rel + 16 <= nb * W) {
+                    st16(D + rel, u.v);
+                } else {
+                    // A chunk the row piece covers in part: its elements one by one.
+#pragma unroll
+                    for (int j = 0; j < E; ++j) {
+                        // Ordinary stores: the chunk's other bytes come from the
+                        // neighbouring tile, and L2 can merge the two before
+                        // writing the line (u8 with destination pitch 8195:
+                        // 1.23 TB/s, against 0.41 non-temporal).
+                        if ((unsigned)(bbf + j) < (unsigned)nb)
+                            *reinterpret_cast<T*>(D + rel + j * W) = u.e[j];
+                    }
+                }
+            }
+        }
+        __syncthreads();   // LDS is reused by the next tile of this workgroup
+    }
+}
+
+// The two forms are separate kernels: the element form's swizzle branch
+// would otherwise set the vector form's register count.
+template <int W, int NB, bool BIG>
+__global__ void __launch_bounds__(256) k_etile_vec(LdsArgs a) {
+    constexpr EtileShape ES = kEtileShapes[etile_index(W)];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[ES.vbytes()];
+    etile_vec_loop<W, NB, BIG>(a, lds);
+}
+
 template <int W, int NB, bool BIG>
 __global__ void __launch_bounds__(256) k_etile(LdsArgs a) {
     constexpr EtileShape ES = kEtileShapes[etile_index(W)];
@@ -79,7 +216,8 @@ __global__ void __launch_bounds__(256) k_etile(LdsArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Launcher.
+// Launcher: the plan picks the form (plain operands of up to 4 bytes take
+// the vector form).
 
 template <int NB, bool BIG>
 hipError_t launch_etile(const Plan& p, const uint8_t* src, uint8_t* dst, hipStream_t st) {
@@ -87,10 +225,20 @@ hipError_t launch_etile(const Plan& p, const uint8_t* src, uint8_t* dst, hipStre
     a.src = src;
     a.dst = dst;
     dim3 grid((unsigned)cap_grid(p.grid, 256)), block(256);
+    const bool vform = a.vform != 0;
     switch (p.w) {
-    case 1: hipLaunchKernelGGL((k_etile<1, NB, BIG>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_etile<2, NB, BIG>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_etile<4, NB, BIG>), grid, block, 0, st, a); break;
+    case 1:
+        if (vform) hipLaunchKernelGGL((k_etile_vec<1, NB, BIG>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_etile<1, NB, BIG>), grid, block, 0, st, a);
+        break;
+    case 2:
+        if (vform) hipLaunchKernelGGL((k_etile_vec<2, NB, BIG>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_etile<2, NB, BIG>), grid, block, 0, st, a);
+        break;
+    case 4:
+        if (vform) hipLaunchKernelGGL((k_etile_vec<4, NB, BIG>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((k_etile<4, NB, BIG>), grid, block, 0, st, a);
+        break;
     case 8: hipLaunchKernelGGL((k_etile<8, NB, BIG>), grid, block, 0, st, a); break;
     default: hipLaunchKernelGGL((k_etile<16, NB, BIG>), grid, block, 0, st, a); break;
     }

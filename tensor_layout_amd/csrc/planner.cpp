@@ -419,14 +419,18 @@ bool count_elements(int rank, const int64_t* ext, int64_t batch, int64_t* out) {
     return true;
 }
 
+static constexpr int kSwzGranuleLog2Cap = 30;
+static constexpr int64_t kPlainGranule = (int64_t)1 << 40;
+
 // granule_s / granule_d: bytes that stay adjacent under each side's swizzle
-// (a vector access must not straddle one); 1 << 30 for a plain side.
+// (a vector access must not straddle one), at most 2^kSwzGranuleLog2Cap for a
+// swizzled side; kPlainGranule for a plain side.
 static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
                       const int64_t* offs, int64_t batch, int src_align, int dst_align, int64_t granule_s,
                       int64_t granule_d) {
     Plan p;
     p.w = w;
-    const bool plain = granule_s >= ((int64_t)1 << 30) && granule_d >= ((int64_t)1 << 30);
+    const bool plain = granule_s == kPlainGranule && granule_d == kPlainGranule;
     const bool vec16 = granule_s >= 16 && granule_d >= 16;
     if (w != 1 && w != 2 && w != 4 && w != 8 && w != 16) {
         p.status = TPL_E_DTYPE_WIDTH;
@@ -757,9 +761,11 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             }
         }
         // Element tiles: a 2-D transpose whose row pitches, bases or swizzle
-        // granules rule out 16-byte vectors still moves through an LDS tile,
-        // one element per access, neighbouring lanes along source rows on the
-        // way in and along destination rows on the way out.
+        // granules rule out the 16-byte vectors of the tile kernel still moves
+        // through an LDS tile: the aligned 16-byte chunks covering each row
+        // piece for plain operands, one element per access otherwise;
+        // neighbouring lanes along source rows on the way in and along
+        // destination rows on the way out.
         const EtileShape* es = etile_shape(w);
         if (es && sa % w == 0 && da % w == 0 && ma.e >= 8 && mb.e >= 8) {
             p.kernel = TPL_KERNEL_ETILE;
@@ -778,14 +784,18 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             l.div_nta = make_fastdiv((uint32_t)std::min<int64_t>(l.nta, 0x7fffffff));
             l.div_ntb = make_fastdiv((uint32_t)std::min<int64_t>(l.ntb, 0x7fffffff));
             set_modes(l.batch, sh, others, no);
-            l.pitch = es->pitch();
+            // Plain operands take the kernel's vector form (16-byte chunks
+            // kept in LDS as read), swizzled ones its element form.
+            const bool vform = plain && w <= 4;
+            l.pitch = vform ? es->rp : es->pitch();
+            l.vform = vform ? 1 : 0;
             p.tile_b = es->tb;
             p.tile_a = es->ta;
             p.pitch = l.pitch;
-            p.P = 1;
+            p.P = vform ? 16 / w : 1;
             p.block = 256;
             p.grid = l.ntiles;
-            p.lds_bytes = es->tb * es->pitch();
+            p.lds_bytes = vform ? es->vbytes() : es->tb * es->pitch();
             // a whole item in one tile is read into LDS before any of it is written
             p.unit_is_item = l.ntb == 1 && l.nta == 1;
             return p;
@@ -826,9 +836,10 @@ Plan plan_gfx950(int w, int rank, const int64_t* ext, const int64_t* ss, const i
         return p;
     }
     const int lw = (w == 1 || w == 2 || w == 4 || w == 8 || w == 16) ? log2_width(w) : 0;
-    const int64_t big = (int64_t)1 << 30;
-    const int64_t gs = zs.bits ? ((int64_t)1 << std::min(30, zs.base + lw)) : big;
-    const int64_t gd = zd.bits ? ((int64_t)1 << std::min(30, zd.base + lw)) : big;
+    // A swizzle whose field starts at byte bit 30 or above still makes its
+    // side swizzled: the kernels without swizzle arithmetic must not take it.
+    const int64_t gs = zs.bits ? ((int64_t)1 << std::min(kSwzGranuleLog2Cap, zs.base + lw)) : kPlainGranule;
+    const int64_t gd = zd.bits ? ((int64_t)1 << std::min(kSwzGranuleLog2Cap, zd.base + lw)) : kPlainGranule;
     Plan p = plan_core(w, rank, ext, ss, ds, offs, batch, src_align, dst_align, gs, gd);
     p.zs = zs;
     p.zd = zd;

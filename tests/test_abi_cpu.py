@@ -656,3 +656,19 @@ def test_counter_hash_ignores_comments_only():
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(c)
     assert '"a // b"' in bench._code_only(a)
+
+
+def test_high_bit_swizzle_never_takes_a_plain_only_kernel():
+    """The record and 16-byte register kernels apply no swizzle.  A swizzle
+    whose field starts at byte bit 30 or above still rewrites offsets of
+    buffers over 1 GiB, so such a side is swizzled, not plain."""
+    n = 1 << 28
+    f3 = ((n, 3), (3, 1), (1, n))                     # float3 records to 3 field arrays
+    assert tpl.tpl_plan(4, *f3).kernel == "rec"
+    for base in (27, 28, 30):                         # byte bits 29, 30, 32
+        assert tpl.tpl_plan(4, *f3, dst_swizzle=(1, base, 1)).kernel not in ("rec", "reg16")
+        assert tpl.tpl_plan(4, *f3, src_swizzle=(1, base, 1)).kernel not in ("rec", "reg16")
+    r16 = ((1 << 26, 8), (8, 1), (1, 1 << 26))         # 16-byte elements, 8-wide rows
+    assert tpl.tpl_plan(16, *r16).kernel == "reg16"
+    for base in (25, 26, 28):
+        assert tpl.tpl_plan(16, *r16, dst_swizzle=(1, base, 1)).kernel not in ("rec", "reg16")

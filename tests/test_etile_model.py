@@ -1,6 +1,8 @@
-"""CPU model of the element-tile kernel's index arithmetic (k_etile), run
-before the GPU does: for small layouts it replays every thread's accesses of
-both phases on numpy buffers, checks each global access against the
+"""CPU model of the element-tile kernel's element form (k_etile on swizzled
+operands; plain operands take the vector form, modelled in
+test_etile_vec_model.py), run before the GPU does: for small layouts it
+replays every thread's accesses of both phases on numpy buffers (the
+swizzle is an address map on top, covered by the GPU parity tests), checks each global access against the
 layout's footprint and each LDS access against the tile, and compares the
 result with the oracle's.  Written from the kernel's description (tiles of
 TB x TA elements in the tile kernel's order, LDS rows of TA elements plus
@@ -92,7 +94,8 @@ def test_etile_model(case):
     x = synth.random_bytes(9, (offs[0] + batch * span_s) * w).copy()
     ref = np.zeros((offs[1] + batch * span_d) * w, dtype=np.uint8)
     oracle.permute(x, ref, w, ext, ss, ds, offs, batch)
-    out, ts, td = model(x, w, ext, ss, ds, offs, batch, p.tile, p.lds_pitch)
+    TB, TA = p.tile
+    out, ts, td = model(x, w, ext, ss, ds, offs, batch, p.tile, TA * w + max(w, 4))
     assert ts <= footprint(ext, ss, batch, span_s, offs[0])
     assert td == footprint(ext, ds, batch, span_d, offs[1])
     assert np.array_equal(out, ref)
@@ -117,3 +120,15 @@ def test_etile_column_reads_hit_distinct_banks(w):
                     b = dw % banks
                     assert used.get(b, dw) == dw, (w, aa, lane)
                     used[b] = dw
+
+
+@pytest.mark.parametrize("w", [1, 2, 4, 8])
+def test_etile_swizzled_plans_take_the_element_form(w):
+    """A swizzle granule under 16 bytes (2^base elements) rules out 16-byte
+    chunks: the plan reports the element form's pitch (row + max(w, 4)).
+    (A 16-byte element's granule is never under 16 bytes.)"""
+    base = 0 if w >= 8 else 1
+    p = tpl.tpl_plan(w, (150, 70), (73, 1), (1, 150), dst_swizzle=(1, base, 3))
+    assert p.ok and p.kernel == "etile", p
+    TB, TA = SHAPES[w]
+    assert tuple(p.tile) == (TB, TA) and p.lds_pitch == TA * w + max(w, 4) and p.P == 1

@@ -1,0 +1,268 @@
+"""CPU model of the element-tile kernel's vector form (plain operands, element
+widths 1-4), run before the GPU does.  For small layouts it replays every
+thread's accesses with the buffers placed at 256-byte aligned addresses (as
+device allocations are), checks each global access and each LDS access, and
+compares the result with the oracle's.  Written from the kernel's
+description, not shared with it:
+
+* tile TB x TA (TB along the destination-contiguous mode b, TA along the
+  source-contiguous mode a), tiles in the tile kernel's order;
+* loading: the source row piece of tile row bb starts lead(bb) = its address
+  mod 16 bytes into a 16-byte aligned chunk; its chunks q with 16 q < lead +
+  na w are read whole and written to LDS at vrow(bb) + 16 q, where vrow(bb) =
+  bb rp + sk (bb >> le); thread t takes chunk t % QS of rows t / QS + i RS,
+  then thread t < TB the extra chunk QS of row t;
+* storing: the destination row piece of tile column aa is cut into the
+  16-byte aligned chunks covering it; a chunk inside the piece is stored
+  whole, a chunk the piece covers in part element by element; element (bb,
+  aa) is read from LDS at vrow(bb) + lead(bb) + aa w.
+
+The bank test replays one wave's LDS accesses on the measured gfx950 pass
+structure and checks that no two lanes of a pass touch different dwords of
+one bank."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from tensor_layout_amd import synth, tpl
+
+NT = 256
+ALIGN = 256
+# w: (TB, TA, rp, sk, le, g)
+VSHAPES = {1: (128, 128, 144, 16, 4, 16), 2: (128, 64, 152, 8, 3, 8), 4: (128, 32, 148, 4, 2, 4)}
+
+
+def vrow(bb, rp, sk, le):
+    return bb * rp + sk * (bb >> le)
+
+
+def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
+    """Replay the vector form on a 2-mode (plus batch) layout; buffers at
+    ALIGN-aligned addresses, element offsets in offs.  Batch items lie one
+    span apart unless item_strides = (source, destination) says otherwise;
+    `out` (the destination buffer) may be given, else one of 0xCD bytes."""
+    TB, TA, rp, sk, le, g = VSHAPES[w]
+    QS, QD = TA * w // 16, TB * w // 16
+    RS, CS = NT // QS, NT // QD
+    a_mode = [i for i, s in enumerate(ss) if s == 1][0]
+    b_mode = [i for i, d in enumerate(ds) if d == 1][0]
+    e_a, e_b = ext[a_mode], ext[b_mode]
+    s_b, d_a = ss[b_mode], ds[a_mode]
+    span_s = 1 + sum((e - 1) * s for e, s in zip(ext, ss))
+    span_d = 1 + sum((e - 1) * d for e, d in zip(ext, ds))
+    istr_s, istr_d = item_strides if item_strides else (span_s, span_d)
+    if out is None:
+        out = np.full((offs[1] + (batch - 1) * istr_d + span_d) * w, 0xCD, dtype=np.uint8)
+    xs = np.zeros(len(x) + 32, dtype=np.uint8)   # 16 bytes of slack on each side for chunk reads
+    xs[16:16 + len(x)] = x
+    chunks, stored = [], []
+    lds_bytes = vrow(TB, rp, sk, le)
+    ntb, nta = -(-e_b // TB), -(-e_a // TA)
+    for item in range(batch):
+        so, d_o = offs[0] + item * istr_s, offs[1] + item * istr_d
+        for tile in range(ntb * nta):
+            tbi, rest = tile % ntb, tile // ntb
+            tq = rest % nta
+            tai = (tq + tbi) % nta
+            b0, a0 = tbi * TB, tai * TA
+            nb, na = min(TB, e_b - b0), min(TA, e_a - a0)
+            lds = np.full(lds_bytes, 0xEE, dtype=np.uint8)
+            written = np.zeros(lds_bytes, dtype=bool)
+            lead_s = {}
+            # phase 1
+            for t in range(NT):
+                slots = [(t // QS + i * RS, t % QS) for i in range(TB // RS)]
+                if t < TB:
+                    slots.append((t, QS))
+                for bb, q in slots:
+                    if bb >= nb:
+                        continue
+                    row = (so + (b0 + bb) * s_b + a0) * w   # byte offset in the source buffer
+                    lead = row % 16                          # buffer base is 16-byte aligned
+                    lead_s[bb] = lead
+                    if q * 16 >= lead + na * w:
+                        continue
+                    A = row - lead + 16 * q
+                    assert A % 16 == 0
+                    # the chunk holds at least one byte of this row piece
+                    assert A < row + na * w and A + 16 > row
+                    chunks.append(A)
+                    l = vrow(bb, rp, sk, le) + 16 * q
+                    assert l % g == 0 and 0 <= l and l + 16 <= lds_bytes
+                    assert l + 16 <= vrow(bb + 1, rp, sk, le)   # stays in its own row
+                    assert not written[l:l + 16].any()
+                    written[l:l + 16] = True
+                    lds[l:l + 16] = xs[16 + A:16 + A + 16]
+            # phase 2
+            for t in range(NT):
+                slots = [(t // QD + i * CS, t % QD) for i in range(TA // CS)]
+                if t < TA:
+                    slots.append((t, QD))
+                for aa, q in slots:
+                    if aa >= na:
+                        continue
+                    D = (d_o + (a0 + aa) * d_a + b0) * w
+                    lead = D % 16
+                    rel = q * 16 - lead
+                    if rel >= nb * w:
+                        continue
+                    assert rel % w == 0
+                    bbf = rel // w
+                    full = rel >= 0 and rel + 16 <= nb * w
+                    for j in range(16 // w):
+                        bb = bbf + j
+                        if bb < 0 or bb >= nb:
+                            assert not full
+                            continue
+                        l = vrow(bb, rp, sk, le) + lead_s[bb] + aa * w
+                        assert l % w == 0 and written[l:l + w].all()
+                        e = D + bb * w
+                        out[e:e + w] = lds[l:l + w]
+                        stored.append(e // w)
+                    if full:
+                        assert (D + rel) % 16 == 0
+    return out, chunks, stored
+
+
+def footprint(ext, strides, batch, span, off):
+    pts = {0}
+    for e, s in zip(ext, strides):
+        pts = {p + i * s for p in pts for i in range(e)}
+    return {off + b * span + p for b in range(batch) for p in pts}
+
+
+CASES = [
+    # w, extents, src strides, dst strides, element offsets, batch
+    (2, (150, 70), (73, 1), (1, 150), (0, 0), 1),        # odd pitch, ragged both ways
+    (2, (300, 140), (141, 1), (1, 300), (3, 0), 1),      # several tiles, source offset
+    (1, (140, 300), (301, 1), (1, 141), (5, 3), 1),      # odd pitches both sides, offsets
+    (1, (260, 130), (133, 1), (1, 260), (0, 7), 2),      # unaligned destination start
+    (4, (130, 40), (41, 1), (1, 133), (1, 0), 2),        # batch of two
+    (4, (200, 90), (93, 1), (1, 203), (2, 1), 1),
+    (2, (40, 20), (21, 1), (1, 40), (0, 0), 3),          # smaller than one tile
+    (2, (16385, 9), (9, 1), (1, 16385), (0, 0), 1),      # destination pitch 16385: partial chunks
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"w{c[0]}_{c[1]}_{c[4]}")
+def test_etile_vector_model(case):
+    w, ext, ss, ds, offs, batch = case
+    p = tpl.tpl_plan(w, ext, ss, ds, offs, batch)
+    assert p.ok and p.kernel == "etile", p
+    TB, TA, rp, sk, le, g = VSHAPES[w]
+    assert tuple(p.tile) == (TB, TA) and p.lds_pitch == rp
+    span_s = 1 + sum((e - 1) * s for e, s in zip(ext, ss))
+    span_d = 1 + sum((e - 1) * d for e, d in zip(ext, ds))
+    x = synth.random_bytes(11, (offs[0] + batch * span_s) * w).copy()
+    ref = np.full((offs[1] + batch * span_d) * w, 0xCD, dtype=np.uint8)
+    oracle.permute(x, ref, w, ext, ss, ds, offs, batch)
+    out, chunks, stored = model(x, w, ext, ss, ds, offs, batch)
+    fp_s = footprint(ext, ss, batch, span_s, offs[0])
+    # every chunk read holds a byte of some source element of the layout
+    for A in set(chunks):
+        assert any((A + k) // w in fp_s for k in range(0, 16, w)), A
+    # every element of the destination footprint is stored exactly once
+    assert sorted(stored) == sorted(footprint(ext, ds, batch, span_d, offs[1]))
+    assert np.array_equal(out, ref)
+
+
+def ways(addrs, width, nbanks):
+    used = {}
+    for a in addrs:
+        for dw in range(a // 4, (a + max(width, 4) - 1) // 4 + 1):
+            used.setdefault(dw % nbanks, set()).add(dw)
+    return max(len(s) for s in used.values())
+
+
+@pytest.mark.parametrize("w", [1, 2, 4])
+@pytest.mark.parametrize("pm", [0, 2, 8, 14])
+def test_etile_vector_lds_is_conflict_free(w, pm):
+    """Measured gfx950 passes: b128 writes 8 lanes, b64 writes 16 lanes (32
+    banks), b32 writes and reads of up to 4 bytes 32 lanes (32 banks); lanes
+    on one dword share it.  pm: the change of
+    a source row's lead per row (the source row pitch in bytes mod 16); the
+    destination is aligned."""
+    if pm % w:
+        pytest.skip("leads are multiples of the element width")
+    TB, TA, rp, sk, le, g = VSHAPES[w]
+    QS, QD = TA * w // 16, TB * w // 16
+    for L0 in sorted({0, (3 * w) % 16}):
+        lead = lambda bb: (L0 + bb * pm) % 16
+        # phase 1: one wave's chunk writes (slot s = lane + 64 i: row s // QS, chunk s % QS)
+        for i in range(TB * QS // 64):
+            slots = [((s // QS), s % QS) for s in range(64 * i, 64 * i + 64)]
+            if g == 16:
+                passes = [[vrow(bb, rp, sk, le) + 16 * q for bb, q in slots[p:p + 8]] for p in range(0, 64, 8)]
+                width = 16
+            elif g == 8:
+                passes = [[vrow(bb, rp, sk, le) + 16 * q + 8 * (((q >> 3) & 1) ^ part) for bb, q in slots[p:p + 16]]
+                          for part in (0, 1) for p in range(0, 64, 16)]
+                width = 8
+            else:
+                passes = [[vrow(bb, rp, sk, le) + 16 * q + part for bb, q in slots[p:p + 32]]
+                          for part in (0, 4, 8, 12) for p in range(0, 64, 32)]
+                width = 4
+            for ps in passes:
+                assert ways(ps, width, 32) == 1, (w, i, ps)
+        # phase 2: element j of one wave's chunks (lane -> chunk lane % QD of column lane // QD)
+        nbanks = 32
+        for c0 in range(0, TA, 64 // QD):
+            for j in range(16 // w):
+                for first in (0, 32):
+                    addrs = []
+                    for lane in range(first, first + 32):
+                        q, aa = lane % QD, c0 + lane // QD
+                        bb = q * (16 // w) + j
+                        if aa < TA and bb < TB:
+                            addrs.append(vrow(bb, rp, sk, le) + lead(bb) + aa * w)
+                    assert ways(addrs, w, nbanks) == 1, (w, pm, L0, c0, j, first)
+
+
+def test_etile_vector_shapes_match_the_library():
+    """The placement constants the model uses are the ones the planner
+    reports; 8-byte elements keep the element form (row + one element)."""
+    for w, (TB, TA, rp, sk, le, g) in VSHAPES.items():
+        p = tpl.tpl_plan(w, (500, 300), (301, 1), (1, 500))
+        assert p.kernel == "etile" and tuple(p.tile) == (TB, TA) and p.lds_pitch == rp and p.P == 16 // w, (w, p)
+    p = tpl.tpl_plan(8, (500, 300), (301, 1), (1, 500))
+    assert p.kernel == "etile" and tuple(p.tile) == (64, 32) and p.lds_pitch == 32 * 8 + 8 and p.P == 1, p
+
+
+def test_etile_vector_lead_sweep_is_conflict_free():
+    """Phase 2 over every tile lead L0 and every per-row lead step pm (the
+    source pitch in bytes mod 16), aligned destination."""
+    for w, (TB, TA, rp, sk, le, g) in VSHAPES.items():
+        QD = TB * w // 16
+        for pm in range(0, 16, w):
+            for L0 in range(0, 16, w):
+                for c0 in range(0, TA, 64 // QD):
+                    for j in range(16 // w):
+                        for first in (0, 32):
+                            addrs = []
+                            for lane in range(first, first + 32):
+                                q, aa = lane % QD, c0 + lane // QD
+                                bb = q * (16 // w) + j
+                                addrs.append(vrow(bb, rp, sk, le) + (L0 + bb * pm) % 16 + aa * w)
+                            assert ways(addrs, w, 32) == 1, (w, pm, L0, c0, j, first)
+
+
+@pytest.mark.parametrize("w,n,pitch,batch,gap,offset", [(1, 100, 101, 7, 0, 0), (2, 60, 61, 9, 3, 1), (4, 30, 33, 4, 5, 2)])
+def test_etile_vector_model_in_place(w, n, pitch, batch, gap, offset):
+    """Square transposes in place, one tile per item, items n pitch + gap
+    elements apart: every chunk an item reads is read before any of the
+    item is written (one workgroup per item), and the buffer ends as the
+    oracle's permutation written over the input (padding and gaps kept)."""
+    item = n * pitch + gap
+    ext, ss, ds = (batch, n, n), (item, pitch, 1), (item, 1, pitch)
+    p = tpl.tpl_plan(w, ext, ss, ds, (offset, offset), 1, geometry=tpl.TPL_GEOM_GFX950_INPLACE)
+    assert p.ok and p.kernel == "etile", p
+    x = synth.random_bytes(13, (offset + batch * item) * w).copy()
+    ref = x.copy()
+    oracle.permute(x, ref, w, ext, ss, ds, (offset, offset), 1)
+    # the model reads the input as it was: each item is one tile, loaded
+    # whole before its stores, and items never write bytes of other items
+    out, _, _ = model(x, w, (n, n), (pitch, 1), (1, pitch), (offset, offset), batch, (item, item), out=x.copy())
+    assert np.array_equal(out, ref)

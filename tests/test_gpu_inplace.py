@@ -75,14 +75,22 @@ CASES = [
     ("u8_1200_two_blocks", 1, 1200, 1200, 1, 0, 0),
     ("16B_330_three_blocks_ragged", 16, 330, 330, 1, 0, 0),
     ("u16_2560_five_blocks_batched", 2, 2560, 2560, 2, 64, 0),
+    # items of one element tile with unaligned rows: the element-tile kernel
+    # reads an item's 16-byte chunks (some shared with the neighbouring
+    # items) before it writes any of the item
+    ("u8_100_pitch101_batched_one_tile", 1, 100, 101, 7, 0, 0),
+    ("u16_60_pitch61_batched_one_tile", 2, 60, 61, 9, 3, 1),
 ]
+
+ONE_TILE = {"u32_64_one_tile": "lds", "u8_100_pitch101_batched_one_tile": "etile",
+            "u16_60_pitch61_batched_one_tile": "etile"}
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
 def test_inplace_square_transpose(case):
     name, w, n, pitch, batch, gap, offset = case
-    # one 64 x 64 tile: the ordinary LDS kernel already reads before it writes
-    kernel = "lds" if name == "u32_64_one_tile" else "swap"
+    # items of one tile: the ordinary tile kernels already read before they write
+    kernel = ONE_TILE.get(name, "swap")
     run_inplace(name, w, n, pitch, batch, gap, offset, expect_kernel=kernel)
 
 

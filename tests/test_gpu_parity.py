@@ -461,8 +461,10 @@ def test_copy_view_matches_oracle():
 
 # ---------------------------------------------------------------------------
 # Element tiles: 2-D transposes that 16-byte vectors cannot serve (odd row
-# pitches, element offsets, small swizzle granules), tiled through LDS one
-# element per access.
+# pitches, element offsets, small swizzle granules), tiled through LDS: plain
+# operands of 1-4 bytes as the aligned 16-byte chunks covering each row piece
+# (the vector form), 8-byte elements and swizzled operands one element per
+# access.
 
 ETILE = [
     # name, w, extents, src strides, dst strides, element offsets, batch, src swizzle, dst swizzle
@@ -474,6 +476,14 @@ ETILE = [
     ("f32_into_8B_granule_swizzle", 4, (64, 96), (96, 1), (1, 64), (0, 0), 2, None, (3, 1, 3)),
     ("u8_from_2B_granule_swizzle", 1, (96, 160), (160, 1), (1, 96), (0, 0), 1, (2, 1, 4), None),
     ("below_one_tile", 4, (12, 20), (21, 1), (1, 13), (0, 0), 5, None, None),
+    # vector form: destination rows not on 16 bytes (partial first and last chunks)
+    ("u8_dst_pitch_odd_only", 1, (300, 256), (256, 1), (1, 301), (0, 0), 1, None, None),
+    ("bf16_dst_pitch_odd_batch", 2, (260, 200), (200, 1), (1, 263), (0, 0), 2, None, None),
+    ("f32_dst_offset_only", 4, (256, 96), (96, 1), (1, 256), (0, 1), 1, None, None),
+    # every lead on both sides, offsets, ragged in both directions
+    ("u8_every_lead_both_sides", 1, (515, 333), (337, 1), (1, 519), (7, 9), 1, None, None),
+    ("bf16_one_past_a_tile", 2, (129, 65), (67, 1), (1, 131), (1, 1), 1, None, None),
+    ("f32_many_tiles_odd", 4, (1000, 700), (701, 1), (1, 1003), (0, 0), 1, None, None),
 ]
 
 
