@@ -72,8 +72,10 @@ enum {
     TPL_KERNEL_SWAP = 6,   /* in-place square transpose: mirrored tile pairs swapped through LDS */
     TPL_KERNEL_REC = 7,    /* records of any size to field rows or back: the dense side as one
                               contiguous block through LDS */
-    TPL_KERNEL_ETILE = 8   /* 2-D tiles through LDS one element per access, for layouts whose
-                              bases, row pitches or swizzle granules rule out 16-byte vectors */
+    TPL_KERNEL_ETILE = 8   /* 2-D tiles through LDS for layouts whose bases, row pitches or
+                              swizzle granules rule out 16-byte vectors: the aligned 16-byte
+                              chunks covering each row (plain operands of 1-4 bytes), else one
+                              element per access */
 };
 
 /*

@@ -74,8 +74,10 @@ __device__ __forceinline__ void etile_loop(const LdsArgs& a, uint8_t* lds) {
 }
 
 // Vector form (plain operands, W <= 4).  Loading, thread t takes chunk
-// t % QS of rows t / QS + i RS, then thread t < TB the one extra chunk of row
-// t that a row piece not starting on 16 bytes reaches into.  A chunk may hold
+// t % QS of rows t / QS + i RS, then thread t < TB the one extra chunk that
+// a row piece not starting on 16 bytes reaches into, of row t / L + (TB / L)
+// (t % L): the L lanes of one LDS write pass (128 / g) take rows TB / L
+// apart, whose extra chunks fall in distinct banks.  A chunk may hold
 // bytes outside the layout; they share its aligned 16 bytes, hence its page,
 // with bytes of the layout, and are never stored.  Storing, thread t takes
 // chunk t % QD of the destination rows (tile columns) t / QD + i CS, then
@@ -89,7 +91,9 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
     constexpr int QS = TA * W / 16, QD = TB * W / 16;   // chunks of a whole source / destination row piece
     constexpr int RS = NT / QS, CS = NT / QD;           // rows / columns per step
     constexpr int NS = TB / RS, ND = TA / CS;           // steps
-    static_assert(NT % QS == 0 && NT % QD == 0 && TB % RS == 0 && TA % CS == 0 && TB <= NT && TA <= NT,
+    constexpr int L = 128 / ES.g;                       // lanes per LDS write pass
+    static_assert(NT % QS == 0 && NT % QD == 0 && TB % RS == 0 && TA % CS == 0 && TB <= NT && TA <= NT &&
+                      TB % L == 0,
                   "tile must tile the threads");
     static_assert(ES.rp >= (QS + 1) * 16 && ES.vrow(1) % ES.g == 0 && ES.rp % ES.g == 0 && ES.sk % ES.g == 0,
                   "LDS rows must hold every chunk at the write piece's alignment");
@@ -115,7 +119,7 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
             bool on[NS + 1];
 #pragma unroll
             for (int i = 0; i <= NS; ++i) {
-                const int bb = i < NS ? r1 + i * RS : t;
+                const int bb = i < NS ? r1 + i * RS : t / L + (TB / L) * (t % L);
                 const int q = i < NS ? q1 : QS;
                 const int lead = (int)((L0 + (uint32_t)bb * pm) & 15);
                 on[i] = (i < NS || t < TB) && bb < nb && q * 16 < lead + na * W;

@@ -11,7 +11,8 @@ description, not shared with it:
   mod 16 bytes into a 16-byte aligned chunk; its chunks q with 16 q < lead +
   na w are read whole and written to LDS at vrow(bb) + 16 q, where vrow(bb) =
   bb rp + sk (bb >> le); thread t takes chunk t % QS of rows t / QS + i RS,
-  then thread t < TB the extra chunk QS of row t;
+  then thread t < TB the extra chunk QS of row t / L + (TB / L) (t % L), L =
+  128 / g being the lanes of one LDS write pass;
 * storing: the destination row piece of tile column aa is cut into the
   16-byte aligned chunks covering it; a chunk inside the piece is stored
   whole, a chunk the piece covers in part element by element; element (bb,
@@ -76,7 +77,8 @@ def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
             for t in range(NT):
                 slots = [(t // QS + i * RS, t % QS) for i in range(TB // RS)]
                 if t < TB:
-                    slots.append((t, QS))
+                    L = 128 // g
+                    slots.append((t // L + (TB // L) * (t % L), QS))
                 for bb, q in slots:
                     if bb >= nb:
                         continue
@@ -207,6 +209,22 @@ def test_etile_vector_lds_is_conflict_free(w, pm):
                 width = 4
             for ps in passes:
                 assert ways(ps, width, 32) == 1, (w, i, ps)
+        # phase 1, the extra chunk of each row: lane t of the first TB takes row
+        # t / L + (TB / L) (t % L), L = 128 / g lanes per write pass
+        L = 128 // g
+        rows = [t // L + (TB // L) * (t % L) for t in range(TB)]
+        assert sorted(rows) == list(range(TB))
+        for p0 in range(0, TB, L):
+            pr = rows[p0:p0 + L]
+            if g == 16:
+                passes = [[vrow(bb, rp, sk, le) + 16 * QS for bb in pr]]
+            elif g == 8:   # chunk QS: (QS >> 3) & 1 picks the half written first
+                h = (QS >> 3) & 1
+                passes = [[vrow(bb, rp, sk, le) + 16 * QS + 8 * (h ^ part) for bb in pr] for part in (0, 1)]
+            else:
+                passes = [[vrow(bb, rp, sk, le) + 16 * QS + part for bb in pr] for part in (0, 4, 8, 12)]
+            for ps in passes:
+                assert ways(ps, g, 32) == 1, (w, "extra", p0)
         # phase 2: element j of one wave's chunks (lane -> chunk lane % QD of column lane // QD)
         nbanks = 32
         for c0 in range(0, TA, 64 // QD):
