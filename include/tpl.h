@@ -138,6 +138,14 @@ typedef struct {
  * disjoint items): then pairs of mirrored tiles are swapped, each pair by one
  * workgroup that reads both tiles before writing either.  Any other overlap
  * returns TPL_E_ALIAS.
+ *
+ * Memory touched: only destination bytes of elements in the layout are
+ * written.  Reads stay between the source layout's first and last byte,
+ * except that a 2-D transpose whose source rows do not start on 16 bytes
+ * (TPL_KERNEL_ETILE, elements of 1-4 bytes) reads each row piece as the
+ * aligned 16-byte blocks covering it: up to 15 bytes before and after a
+ * piece, never outside those aligned blocks (so never on another page),
+ * and never stored.
  * Returns a tpl_status; thread-safe.
  */
 int tpl_permute(const void *src, void *dst, int dtype_bytes, int rank,
