@@ -100,6 +100,45 @@ def record_case(rng):
     return w, ext, ss, ds, offs, batch
 
 
+def random_unaligned_transpose(rng):
+    """A 2-D transpose (plus batch) whose rows miss 16-byte alignment on one
+    side or both: random width, extents, row pitches, element offsets,
+    batch with or without gaps between items."""
+    w = int(rng.choice([1, 2, 4, 8]))
+    e_b = int(rng.integers(8, 700))
+    e_a = int(rng.integers(8, 700))
+    while e_a * e_b * w > (2 << 20):
+        e_a, e_b = max(8, e_a // 2), max(8, e_b // 2)
+    ps = e_a + int(rng.choice([0, 1, 2, 3, 5, 7, 16, 17]))
+    pd = e_b + int(rng.choice([0, 1, 3, 8, 9, 15]))
+    offs = (int(rng.integers(0, 20)), int(rng.choice([0, 0, 1, 4, 13])))
+    batch = int(rng.choice([1, 1, 2, 3]))
+    ext, ss, ds = (e_b, e_a), (ps, 1), (1, pd)
+    if batch > 1 and rng.random() < 0.5:
+        # items further apart than their span
+        span_s, span_d = (e_b - 1) * ps + e_a, (e_a - 1) * pd + e_b
+        gs, gd = int(rng.integers(0, 40)), int(rng.integers(0, 40))
+        ext, ss, ds = (batch, e_b, e_a), (span_s + gs, ps, 1), (span_d + gd, 1, pd)
+        batch = 1
+    return w, ext, ss, ds, offs, batch
+
+
+def test_random_unaligned_transposes_match_oracle():
+    """The element-tile kernel's two forms (16-byte chunks for 1-4 byte
+    elements, one element per access for 8-byte ones) on random unaligned
+    layouts, byte for byte against the oracle."""
+    rng = np.random.default_rng(1202)
+    kernels = collections.Counter()
+    for t in range(60 * SCALE):
+        w, ext, ss, ds, offs, batch = random_unaligned_transpose(rng)
+        p = tpl.tpl_plan(w, ext, ss, ds, offs, batch)
+        assert p.ok, (t, p)
+        kernels[(p.kernel, w)] += 1
+        run_case(f"unaligned_{t}", w, ext, ss, ds, offs, batch, seed=1000 + t)
+    print("kernel mix:", dict(kernels), flush=True)
+    assert sum(n for (k, w), n in kernels.items() if k == "etile" and w <= 4) >= 30 * SCALE
+
+
 def test_random_record_layouts_match_oracle():
     rng = np.random.default_rng(7)
     kernels = collections.Counter()
