@@ -167,7 +167,8 @@ struct EtileShape {
     constexpr TPL_HD int unit() const { return w < 4 ? 4 : w; }
     constexpr TPL_HD int pitch() const { return ta * w + unit(); }
     constexpr TPL_HD int vrow(int bb) const { return bb * rp + sk * (bb >> le); }
-    constexpr TPL_HD int vbytes() const { return vrow(tb); }
+    // rows: TB and up to 16 / w - 1 more (destination rows not on 16 bytes)
+    constexpr TPL_HD int vbytes() const { return vrow(tb + 16 / w - 1); }
 };
 
 // One shape per width: TA elements of a source row make 128 or 256 bytes, TB
@@ -207,8 +208,9 @@ struct LdsArgs {
     int64_t nbl;
     FastDiv div_nbl;
     int32_t scalar;
-    // Element tiles only: 1 for the vector form (16-byte chunks kept in LDS
-    // as read), 0 for the element form.
+    // Element tiles only: 0 for the element form; the vector form (16-byte
+    // chunks kept in LDS as read) 1 with every destination row on 16 bytes,
+    // 2 with destination rows whose tile ranges shift to 16-byte boundaries.
     int32_t vform;
     Swz zs, zd;          // operand swizzles (byte form)
 };

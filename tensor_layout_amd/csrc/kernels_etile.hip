@@ -80,10 +80,17 @@ __device__ __forceinline__ void etile_loop(const LdsArgs& a, uint8_t* lds) {
 // apart, whose extra chunks fall in distinct banks.  A chunk may hold
 // bytes outside the layout; they share its aligned 16 bytes, hence its page,
 // with bytes of the layout, and are never stored.  Storing, thread t takes
-// chunk t % QD of the destination rows (tile columns) t / QD + i CS, then
-// thread t < TA the extra chunk of column t; 16 neighbouring lanes (8 for
-// bytes, 32 for 4-byte elements) cover a column's row piece.
-template <int W, int NB, bool BIG>
+// chunk t % QD of the destination rows (tile columns) t / QD + i CS; 16
+// neighbouring lanes (8 for bytes, 32 for 4-byte elements) cover a column's
+// row piece.  A column owns the rows [delta, delta + TB) from b0, delta being
+// the elements from its destination row's address at b0 to the next 16-byte
+// boundary, so that its chunks are whole; the item's first tile also owns
+// rows [0, delta), stored by thread t < TA for column t.  When a column has
+// delta > 0 the tile loads TB + 16 / W - 1 rows, the last ones in one more
+// step.  Partial chunks, stored element by element, are left only at an
+// item's first and last rows.  SHIFT = false compiles the case where every
+// destination row is on 16 bytes (delta = 0, TB rows): fewer registers.
+template <int W, int NB, bool BIG, bool SHIFT>
 __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
     typedef typename Elem<W>::type T;
     constexpr EtileShape ES = kEtileShapes[etile_index(W)];
@@ -92,8 +99,9 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
     constexpr int RS = NT / QS, CS = NT / QD;           // rows / columns per step
     constexpr int NS = TB / RS, ND = TA / CS;           // steps
     constexpr int L = 128 / ES.g;                       // lanes per LDS write pass
+    constexpr int XR = E - 1;                           // rows loaded past TB for shifted columns
     static_assert(NT % QS == 0 && NT % QD == 0 && TB % RS == 0 && TA % CS == 0 && TB <= NT && TA <= NT &&
-                      TB % L == 0,
+                      TB % L == 0 && XR * (QS + 1) <= NT,
                   "tile must tile the threads");
     static_assert(ES.rp >= (QS + 1) * 16 && ES.vrow(1) % ES.g == 0 && ES.rp % ES.g == 0 && ES.sk % ES.g == 0,
                   "LDS rows must hold every chunk at the write piece's alignment");
@@ -113,16 +121,40 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
         const uint8_t* s0 = a.src + (so + b0 * a.s_b + a0) * W;   // row 0 of the tile's source piece
         const uint32_t L0 = (uint32_t)(uintptr_t)s0 & 15;
         const int64_t srow = a.s_b * W;
+        // rows to load: XR more when some column's destination row is not on 16 bytes
+        const bool shifted =
+            SHIFT && (((uint32_t)(uintptr_t)(a.dst + (d_o + a0 * a.d_a + b0) * W) | (uint32_t)(a.d_a * W)) & 15) != 0;
+        const int nl = shifted ? (int)(a.e_b - b0 < TB + XR ? a.e_b - b0 : TB + XR) : nb;
+        // One 16-byte chunk into LDS at byte l, chunk slot q of its row (pieces of g bytes).
+        auto put = [&](int at, int q, const u32x4& v) {
+            uint8_t* l = lds + at;
+            if constexpr (ES.g == 16) {
+                *reinterpret_cast<u32x4*>(l) = v;
+            } else if constexpr (ES.g == 8) {
+                // Lanes 8 chunks apart write their halves in opposite order.
+                const u32x2 lo = {v.x, v.y}, hi = {v.z, v.w};
+                const bool h = (q >> 3) & 1;
+                *reinterpret_cast<u32x2*>(l + (h ? 8 : 0)) = h ? hi : lo;
+                *reinterpret_cast<u32x2*>(l + (h ? 0 : 8)) = h ? lo : hi;
+            } else {
+                uint32_t* d = reinterpret_cast<uint32_t*>(l);
+                d[0] = v.x;
+                d[1] = v.y;
+                d[2] = v.z;
+                d[3] = v.w;
+            }
+        };
         {
             u32x4 v[NS + 1];
             int at_lds[NS + 1];
             bool on[NS + 1];
 #pragma unroll
             for (int i = 0; i <= NS; ++i) {
+                // steps: NS of whole row pieces, then the extra chunks of rows < TB
                 const int bb = i < NS ? r1 + i * RS : t / L + (TB / L) * (t % L);
                 const int q = i < NS ? q1 : QS;
                 const int lead = (int)((L0 + (uint32_t)bb * pm) & 15);
-                on[i] = (i < NS || t < TB) && bb < nb && q * 16 < lead + na * W;
+                on[i] = (i < NS || t < TB) && bb < nl && q * 16 < lead + na * W;
                 at_lds[i] = ES.vrow(bb) + q * 16;
                 if (on[i]) {
                     // The first and last chunk of a row piece may hold bytes
@@ -136,62 +168,70 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
             }
 #pragma unroll
             for (int i = 0; i <= NS; ++i) {
-                if (!on[i]) continue;
-                uint8_t* l = lds + at_lds[i];
-                if constexpr (ES.g == 16) {
-                    *reinterpret_cast<u32x4*>(l) = v[i];
-                } else if constexpr (ES.g == 8) {
-                    // Lanes 8 chunks apart write their halves in opposite order.
-                    const int q = i < NS ? q1 : QS;
-                    const u32x2 lo = {v[i].x, v[i].y}, hi = {v[i].z, v[i].w};
-                    const bool h = (q >> 3) & 1;
-                    *reinterpret_cast<u32x2*>(l + (h ? 8 : 0)) = h ? hi : lo;
-                    *reinterpret_cast<u32x2*>(l + (h ? 0 : 8)) = h ? lo : hi;
-                } else {
-                    uint32_t* d = reinterpret_cast<uint32_t*>(l);
-                    d[0] = v[i].x;
-                    d[1] = v[i].y;
-                    d[2] = v[i].z;
-                    d[3] = v[i].w;
-                }
+                if (on[i]) put(at_lds[i], i < NS ? q1 : QS, v[i]);
             }
+        }
+        if (shifted && t < XR * (QS + 1)) {
+            // rows TB.. of shifted columns: thread t takes chunk t % (QS + 1) of
+            // row TB + t / (QS + 1); the next tile reads them too (ordinary loads)
+            const int bb = TB + t / (QS + 1), q = t % (QS + 1);
+            const int lead = (int)((L0 + (uint32_t)bb * pm) & 15);
+            if (bb < nl && q * 16 < lead + na * W)
+                put(ES.vrow(bb) + q * 16, q, *reinterpret_cast<const u32x4*>(s0 + bb * srow - lead + q * 16));
         }
         __syncthreads();
         {
             uint8_t* d0 = a.dst + (d_o + a0 * a.d_a + b0) * W;   // the tile's destination row 0
             const int64_t drow = a.d_a * W;
+            const int rows = (int)(a.e_b - b0 < TB + XR ? a.e_b - b0 : TB + XR);   // of the item, from b0
 #pragma unroll
             for (int i = 0; i <= ND; ++i) {
                 const int aa = i < ND ? c2 + i * CS : t;
-                const int q = i < ND ? q2 : QD;
                 if (!((i < ND || t < TA) && aa < na)) continue;
                 uint8_t* D = d0 + aa * drow;
-                const int lead = (int)((uint32_t)(uintptr_t)D & 15);
-                const int rel = q * 16 - lead;   // chunk start, bytes from the row piece's start
-                if (rel >= nb * W) continue;
-                const int bbf = rel / W;         // exact: lead is a multiple of W
+                int rel, lo, hi;                   // chunk start (bytes from D) and the rows [lo, hi) stored
+                if constexpr (SHIFT) {
+                    const int lead = (int)((uint32_t)(uintptr_t)D & 15);
+                    const int dw = (16 - lead) & 15;   // bytes to the next 16-byte boundary: delta W
+                    if (i < ND) {
+                        rel = dw + q2 * 16;
+                        lo = dw / W;
+                        hi = lo + TB < rows ? lo + TB : rows;
+                    } else {
+                        if (tbi != 0 || lead == 0) continue;   // the item's first rows [0, delta)
+                        rel = -lead;
+                        lo = 0;
+                        hi = dw / W < rows ? dw / W : rows;
+                    }
+                } else {
+                    if (i == ND) continue;
+                    rel = q2 * 16;
+                    lo = 0;
+                    hi = nb;
+                }
+                if (rel >= hi * W) continue;
+                const int bbf = rel / W;           // exact: lead is a multiple of W
                 union {
                     u32x4 v;
                     T e[E];
                 } u;
 #pragma unroll
                 for (int j = 0; j < E; ++j) {
-                    // rows outside the piece read row 0 (a partial chunk stores no such element)
-                    const int bb = (unsigned)(bbf + j) < (unsigned)nb ? bbf + j : 0;
+                    // rows not stored read row lo (a partial chunk stores no such element)
+                    const int bb = (unsigned)(bbf + j - lo) < (unsigned)(hi - lo) ? bbf + j : lo;
                     const int ls = (int)((L0 + (uint32_t)bb * pm) & 15);
                     u.e[j] = *reinterpret_cast<const T*>(lds + ES.vrow(bb) + ls + aa * W);
                 }
-                if (rel >= 0 && rel + 16 <= nb * W) {
+                if (rel >= lo * W && rel + 16 <= hi * W) {
                     st16(D + rel, u.v);
                 } else {
                     // A chunk the row piece covers in part: its elements one by one.
 #pragma unroll
                     for (int j = 0; j < E; ++j) {
-                        // Ordinary stores: the chunk's other bytes come from the
-                        // neighbouring tile, and L2 can merge the two before
-                        // writing the line (u8 with destination pitch 8195:
-                        // 1.23 TB/s, against 0.41 non-temporal).
-                        if ((unsigned)(bbf + j) < (unsigned)nb)
+                        // Ordinary stores: the chunk's other bytes may come
+                        // from another workgroup (a neighbouring item), and L2
+                        // can merge the two before writing the line.
+                        if ((unsigned)(bbf + j - lo) < (unsigned)(hi - lo))
                             *reinterpret_cast<T*>(D + rel + j * W) = u.e[j];
                     }
                 }
@@ -203,11 +243,11 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
 
 // The two forms are separate kernels: the element form's swizzle branch
 // would otherwise set the vector form's register count.
-template <int W, int NB, bool BIG>
+template <int W, int NB, bool BIG, bool SHIFT>
 __global__ void __launch_bounds__(256) k_etile_vec(LdsArgs a) {
     constexpr EtileShape ES = kEtileShapes[etile_index(W)];
-    __shared__ __attribute__((aligned(16))) uint8_t lds[ES.vbytes()];
-    etile_vec_loop<W, NB, BIG>(a, lds);
+    __shared__ __attribute__((aligned(16))) uint8_t lds[SHIFT ? ES.vbytes() : ES.vrow(ES.tb)];
+    etile_vec_loop<W, NB, BIG, SHIFT>(a, lds);
 }
 
 template <int W, int NB, bool BIG>
@@ -229,23 +269,20 @@ hipError_t launch_etile(const Plan& p, const uint8_t* src, uint8_t* dst, hipStre
     a.src = src;
     a.dst = dst;
     dim3 grid((unsigned)cap_grid(p.grid, 256)), block(256);
-    const bool vform = a.vform != 0;
+#define TPL_ETILE_CASE(W_)                                                                   \
+    case W_:                                                                                 \
+        if (a.vform == 1) hipLaunchKernelGGL((k_etile_vec<W_, NB, BIG, false>), grid, block, 0, st, a); \
+        else if (a.vform == 2) hipLaunchKernelGGL((k_etile_vec<W_, NB, BIG, true>), grid, block, 0, st, a); \
+        else hipLaunchKernelGGL((k_etile<W_, NB, BIG>), grid, block, 0, st, a);              \
+        break;
     switch (p.w) {
-    case 1:
-        if (vform) hipLaunchKernelGGL((k_etile_vec<1, NB, BIG>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_etile<1, NB, BIG>), grid, block, 0, st, a);
-        break;
-    case 2:
-        if (vform) hipLaunchKernelGGL((k_etile_vec<2, NB, BIG>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_etile<2, NB, BIG>), grid, block, 0, st, a);
-        break;
-    case 4:
-        if (vform) hipLaunchKernelGGL((k_etile_vec<4, NB, BIG>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_etile<4, NB, BIG>), grid, block, 0, st, a);
-        break;
+        TPL_ETILE_CASE(1)
+        TPL_ETILE_CASE(2)
+        TPL_ETILE_CASE(4)
     case 8: hipLaunchKernelGGL((k_etile<8, NB, BIG>), grid, block, 0, st, a); break;
     default: hipLaunchKernelGGL((k_etile<16, NB, BIG>), grid, block, 0, st, a); break;
     }
+#undef TPL_ETILE_CASE
     return hipGetLastError();
 }
 

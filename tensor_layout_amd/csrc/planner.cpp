@@ -788,14 +788,14 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             // kept in LDS as read), swizzled ones its element form.
             const bool vform = plain && w <= 4;
             l.pitch = vform ? es->rp : es->pitch();
-            l.vform = vform ? 1 : 0;
+            l.vform = !vform ? 0 : dst_ok ? 1 : 2;
             p.tile_b = es->tb;
             p.tile_a = es->ta;
             p.pitch = l.pitch;
             p.P = vform ? 16 / w : 1;
             p.block = 256;
             p.grid = l.ntiles;
-            p.lds_bytes = vform ? es->vbytes() : es->tb * es->pitch();
+            p.lds_bytes = !vform ? es->tb * es->pitch() : dst_ok ? es->vrow(es->tb) : es->vbytes();
             // a whole item in one tile is read into LDS before any of it is written
             p.unit_is_item = l.ntb == 1 && l.nta == 1;
             return p;

@@ -13,10 +13,16 @@ description, not shared with it:
   bb rp + sk (bb >> le); thread t takes chunk t % QS of rows t / QS + i RS,
   then thread t < TB the extra chunk QS of row t / L + (TB / L) (t % L), L =
   128 / g being the lanes of one LDS write pass;
-* storing: the destination row piece of tile column aa is cut into the
-  16-byte aligned chunks covering it; a chunk inside the piece is stored
-  whole, a chunk the piece covers in part element by element; element (bb,
-  aa) is read from LDS at vrow(bb) + lead(bb) + aa w.
+* storing: tile column aa owns destination rows [delta, delta + TB) (from
+  b0; clipped to the item), delta = the elements from its destination row's
+  address at b0 to the next 16-byte boundary, so that its chunks are whole;
+  the item's first tile also owns rows [0, delta), stored by thread aa of
+  the extra step.  When some column has delta > 0 the tile loads TB + 16/w
+  - 1 rows: the extra rows TB.. as one more step, thread f taking chunk f %
+  (QS + 1) of row TB + f / (QS + 1).  A chunk inside the owned rows is
+  stored whole, one it covers in part (the item's first or last rows)
+  element by element; element (bb, aa) is read from LDS at vrow(bb) +
+  lead(bb) + aa w.
 
 The bank test replays one wave's LDS accesses on the measured gfx950 pass
 structure and checks that no two lanes of a pass touch different dwords of
@@ -60,7 +66,8 @@ def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
     xs = np.zeros(len(x) + 32, dtype=np.uint8)   # 16 bytes of slack on each side for chunk reads
     xs[16:16 + len(x)] = x
     chunks, stored = [], []
-    lds_bytes = vrow(TB, rp, sk, le)
+    E = 16 // w
+    lds_bytes = vrow(TB + E - 1, rp, sk, le)
     ntb, nta = -(-e_b // TB), -(-e_a // TA)
     for item in range(batch):
         so, d_o = offs[0] + item * istr_s, offs[1] + item * istr_d
@@ -70,6 +77,9 @@ def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
             tai = (tq + tbi) % nta
             b0, a0 = tbi * TB, tai * TA
             nb, na = min(TB, e_b - b0), min(TA, e_a - a0)
+            D0 = (d_o + a0 * d_a + b0) * w
+            shifted = D0 % 16 != 0 or (d_a * w) % 16 != 0
+            nl = min(TB + E - 1, e_b - b0) if shifted else nb   # rows loaded
             lds = np.full(lds_bytes, 0xEE, dtype=np.uint8)
             written = np.zeros(lds_bytes, dtype=bool)
             lead_s = {}
@@ -79,8 +89,10 @@ def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
                 if t < TB:
                     L = 128 // g
                     slots.append((t // L + (TB // L) * (t % L), QS))
+                if t < (E - 1) * (QS + 1):
+                    slots.append((TB + t // (QS + 1), t % (QS + 1)))
                 for bb, q in slots:
-                    if bb >= nb:
+                    if bb >= nl:
                         continue
                     row = (so + (b0 + bb) * s_b + a0) * w   # byte offset in the source buffer
                     lead = row % 16                          # buffer base is 16-byte aligned
@@ -108,15 +120,23 @@ def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
                         continue
                     D = (d_o + (a0 + aa) * d_a + b0) * w
                     lead = D % 16
-                    rel = q * 16 - lead
-                    if rel >= nb * w:
+                    delta = ((16 - lead) % 16) // w
+                    if q < QD:     # owned rows [delta, delta + TB), clipped to the item
+                        rel, lo, hi = (16 - lead) % 16 + 16 * q, delta, min(delta + TB, e_b - b0)
+                    else:          # the item's first rows [0, delta)
+                        if tbi != 0 or lead == 0:
+                            continue
+                        rel, lo, hi = -lead, 0, min(delta, e_b - b0)
+                    if rel >= hi * w:
                         continue
-                    assert rel % w == 0
+                    assert rel % w == 0 and hi <= nl
                     bbf = rel // w
-                    full = rel >= 0 and rel + 16 <= nb * w
+                    full = rel >= lo * w and rel + 16 <= hi * w
+                    # partial chunks only at the item's first or last rows
+                    assert full or q == QD or hi == e_b - b0, (tile, aa, q)
                     for j in range(16 // w):
                         bb = bbf + j
-                        if bb < 0 or bb >= nb:
+                        if bb < lo or bb >= hi:
                             assert not full
                             continue
                         l = vrow(bb, rp, sk, le) + lead_s[bb] + aa * w
