@@ -24,6 +24,22 @@ __device__ __forceinline__ void st16(uint8_t* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
+// A 16-byte store with device scope (sc1) besides the non-temporal hint.  A
+// plain 512 MiB copy measured 6.77 TB/s that way against 6.66 with the hint
+// alone (MI355X); across the kernels it helps the quad kernel (+1-2 % on the
+// scale-factor and record tiles) and costs the LDS-tile and record kernels
+// up to 4 % on some layouts, so only the quad kernel and the 16-byte run
+// copy (the plain copy the others are measured against) use it.  No builtin
+// sets sc1 on a global store, hence the asm.  A store of more than 8 bytes
+// reads its data registers after issue, and the compiler cannot see into the
+// asm to keep a following VALU write to them 2 wait states away, so the asm
+// ends with that wait itself (s_nop 1, what the compiler emits after its own
+// 16-byte stores).  The memory clobber keeps the store in program order with
+// every other memory access.
+__device__ __forceinline__ void st16_dev(uint8_t* p, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 1" ::"v"(p), "v"(v) : "memory");
+}
+
 // base + P, or base + swz(P) for a swizzled operand.
 template <bool SWZ>
 __device__ __forceinline__ uint8_t* at(const uint8_t* base, int64_t p, const Swz& z) {

@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(64) k_quad(QuadArgs a) {
         const u32x4 y = columns_from_rows<W>(transpose4<WIDE>(v, r, lane));
         if (act) {
             if constexpr (!SPLIT) {
-                st16(at<SWZ>(a.dst, dofs, a.zd), y);
+                st16_dev(at<SWZ>(a.dst, dofs, a.zd), y);
             } else if constexpr (W == 2) {
                 __builtin_nontemporal_store(u32x2{y.x, y.y}, reinterpret_cast<u32x2*>(at<SWZ>(a.dst, dofs, a.zd)));
                 __builtin_nontemporal_store(u32x2{y.z, y.w},

@@ -48,7 +48,8 @@ __global__ void __launch_bounds__(64) k_copy(CopyArgs a) {
         int64_t so, d_o;
         modes_offsets<NB, BIG>(a.rows, row, so, d_o);
         const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(at<SWZ>(a.src, so * a.w + c * V, a.zs)));
-        __builtin_nontemporal_store(v, reinterpret_cast<T*>(at<SWZ>(a.dst, d_o * a.w + c * V, a.zd)));
+        if constexpr (V == 16) st16_dev(at<SWZ>(a.dst, d_o * a.w + c * V, a.zd), v);   // device-scope store
+        else __builtin_nontemporal_store(v, reinterpret_cast<T*>(at<SWZ>(a.dst, d_o * a.w + c * V, a.zd)));
     }
 }
 
