@@ -89,7 +89,8 @@ __device__ __forceinline__ void etile_loop(const LdsArgs& a, uint8_t* lds) {
 // delta > 0 the tile loads TB + 16 / W - 1 rows, the last ones in one more
 // step.  Partial chunks, stored element by element, are left only at an
 // item's first and last rows.  SHIFT = false compiles the case where every
-// destination row is on 16 bytes (delta = 0, TB rows): fewer registers.
+// destination row is on 16 bytes (delta = 0, TB rows) without the shift
+// arithmetic.
 template <int W, int NB, bool BIG, bool SHIFT>
 __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
     typedef typename Elem<W>::type T;
@@ -125,7 +126,8 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
         const bool shifted =
             SHIFT && (((uint32_t)(uintptr_t)(a.dst + (d_o + a0 * a.d_a + b0) * W) | (uint32_t)(a.d_a * W)) & 15) != 0;
         const int nl = shifted ? (int)(a.e_b - b0 < TB + XR ? a.e_b - b0 : TB + XR) : nb;
-        // One 16-byte chunk into LDS at byte l, chunk slot q of its row (pieces of g bytes).
+        // One 16-byte chunk into LDS at byte offset `at`, chunk slot q of its row,
+        // written in pieces of g bytes.
         auto put = [&](int at, int q, const u32x4& v) {
             uint8_t* l = lds + at;
             if constexpr (ES.g == 16) {
