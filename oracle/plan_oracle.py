@@ -41,7 +41,7 @@ Readings where the pages are silent (each listed in the design notes):
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import List, Optional, Sequence, Tuple
+from typing import List, Sequence, Tuple
 
 # Decline reasons, in the order of the pages' predicate list ("What it accepts").
 REASON_WIDTH = "unsupported dtype byte width"
@@ -53,22 +53,18 @@ REASON_DTYPE = "dtype mismatch"
 
 @dataclass
 class Geometry:
-    """Bank model used by the k search.
+    """Bank model used by the k search: the pages' shared memory.
 
-    One unrolled step of the whole wave is split into passes of
+    One unrolled step of the whole warp is split into passes of
     ``pass_lanes(w)`` consecutive lanes; inside one pass no two lanes may use
-    the same bank (unless ``same_word_ok`` and they touch the same word).
+    the same bank, even when they touch the same word.
     """
 
     lanes: int = 32          # lanes that run one unrolled step together
     banks: int = 32          # number of banks
     bank_bytes: int = 4      # bytes per bank
-    same_word_ok: bool = False  # two lanes reading the same word do not conflict
-    pass_table: Optional[dict] = None  # access width in bytes -> lanes per pass
 
     def pass_lanes(self, w: int) -> int:
-        if self.pass_table is not None:
-            return self.pass_table[max(w, self.bank_bytes)]
         words = max(1, w // self.bank_bytes)
         return max(1, min(self.lanes, self.banks // words))
 
@@ -178,17 +174,14 @@ def step_conflict_free(offsets: Sequence[int], w: int, geom: Geometry) -> bool:
     words = max(1, w // geom.bank_bytes)
     lanes_per_pass = geom.pass_lanes(w)
     for p0 in range(0, len(offsets), lanes_per_pass):
-        seen = {}
+        seen = set()
         for o in offsets[p0:p0 + lanes_per_pass]:
-            byte = o * w
-            word0 = byte // geom.bank_bytes
+            word0 = (o * w) // geom.bank_bytes
             for k in range(words):
-                word = word0 + k
-                bank = word % geom.banks
+                bank = (word0 + k) % geom.banks
                 if bank in seen:
-                    if not (geom.same_word_ok and seen[bank] == word):
-                        return False
-                seen[bank] = word
+                    return False
+                seen.add(bank)
     return True
 
 
