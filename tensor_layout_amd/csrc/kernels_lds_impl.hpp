@@ -98,11 +98,13 @@ hipError_t launch_lds_width(const Plan& p, const LdsArgs& a, hipStream_t st) {
     }
     if constexpr (W == 2) {
         TPL_LDS_SHAPE(2, 256, 64, 2)
+        TPL_LDS_SHAPE(2, 128, 128, 4)
         TPL_LDS_SHAPE(2, 128, 64, 2)
         TPL_LDS_SHAPE(2, 32, 64, 2)
     }
     if constexpr (W == 4) {
         TPL_LDS_SHAPE(4, 64, 64, 2)
+        TPL_LDS_SHAPE(4, 32, 256, 2)
         TPL_LDS_SHAPE(4, 32, 32, 2)
     }
     if constexpr (W == 8) {

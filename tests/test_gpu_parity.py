@@ -546,23 +546,28 @@ def test_rank8_permutations_match_oracle(case):
 # ---------------------------------------------------------------------------
 # Every tile shape the tiled transpose instantiates, picked by extents just
 # past the shape (ragged edges on both modes), as one item and as two items
-# of a batch mode.
+# of a batch mode.  The short-destination shapes are picked when the
+# source-contiguous extent is at least four times the destination-contiguous
+# one, so their cases take a long source-contiguous mode.
 
 LDS_SHAPES = [(1, 128, 128), (1, 64, 128), (2, 256, 64), (2, 128, 64), (2, 32, 64), (4, 64, 64), (4, 32, 32),
-              (8, 32, 64), (8, 16, 32), (16, 64, 16), (16, 16, 64), (16, 16, 16)]
+              (8, 32, 64), (8, 16, 32), (16, 64, 16), (16, 16, 64), (16, 16, 16),
+              (2, 128, 128, "short_dst"), (4, 32, 256, "short_dst")]
 
 
-def _shape_case(w, tb, ta):
+def _shape_case(w, tb, ta, short_dst=False):
     eb, ea = tb + 3, ta + 5
+    if short_dst:
+        ea = max(ea, 4 * eb)
     pa = -(-ea * w // 16) * 16 // w    # rows padded to whole 16-byte chunks
     pb = -(-eb * w // 16) * 16 // w
     return eb, ea, pa, pb
 
 
-@pytest.mark.parametrize("shape", LDS_SHAPES, ids=lambda s: f"w{s[0]}_{s[1]}x{s[2]}")
+@pytest.mark.parametrize("shape", LDS_SHAPES, ids=lambda s: f"w{s[0]}_{s[1]}x{s[2]}" + ("_short_dst" if len(s) > 3 else ""))
 def test_every_lds_tile_shape(shape):
-    w, tb, ta = shape
-    eb, ea, pa, pb = _shape_case(w, tb, ta)
+    w, tb, ta = shape[:3]
+    eb, ea, pa, pb = _shape_case(w, tb, ta, len(shape) > 3)
     ext, ss, ds = (eb, ea), (pa, 1), (1, pb)
     p = tpl.tpl_plan(w, ext, ss, ds)
     assert p.kernel == "lds" and tuple(p.tile) == (tb, ta), p
