@@ -34,10 +34,10 @@ PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 2 << 30      # src+dst bytes cycled through per rotation
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # The sources of the profiled kernels and their planner (not the staged
-# entry or the bank probe, which the counters do not cover).
+# entry, which the counters do not cover).
 _CSRC = os.path.join(ROOT, "tensor_layout_amd", "csrc")
 KERNEL_SOURCES = sorted(os.path.join(_CSRC, f) for f in os.listdir(_CSRC)
-                        if f.endswith((".hip", ".hpp", ".cpp")) and f not in ("staged.hip", "lds_probe.hip"))
+                        if f.endswith((".hip", ".hpp", ".cpp")) and f != "staged.hip")
 
 
 def _code_only(text: str) -> str:

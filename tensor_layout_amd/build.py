@@ -28,10 +28,6 @@ FLAGS = [
 ]
 
 
-PROBE = os.path.join(HERE, "lds_probe")
-PROBE_FLAGS = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
-
-
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -51,17 +47,15 @@ CLIENT = os.path.join(ROOT, "tests", "c_abi", "abi_client")
 
 
 def build(verbose: bool = False) -> str:
-    """Build libtpl.so, the LDS bank-geometry probe and the C ABI test client (all in-tree).
+    """Build libtpl.so and the C ABI test client (both in-tree).
 
-    Every source is compiled to an object on its own (in parallel, with the
-    probe alongside), then the objects are linked."""
+    Every source is compiled to an object on its own (in parallel), then the
+    objects are linked."""
     compile_flags = [f for f in FLAGS if f != "-shared"]
     objdir = tempfile.mkdtemp(prefix="tpl_build_")
     try:
         objs = [os.path.join(objdir, s + ".o") for s in SOURCES]
-        ptmp = PROBE + ".tmp"
         jobs = [[HIPCC] + compile_flags + ["-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
-        jobs.append([HIPCC] + PROBE_FLAGS + [os.path.join(CSRC, "lds_probe.hip"), "-o", ptmp])
         workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
         with cf.ThreadPoolExecutor(max_workers=workers) as ex:
             for f in [ex.submit(_run, j, verbose) for j in jobs]:
@@ -69,7 +63,6 @@ def build(verbose: bool = False) -> str:
         tmp = LIB + ".tmp"
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
         os.replace(tmp, LIB)
-        os.replace(ptmp, PROBE)
     finally:
         shutil.rmtree(objdir, ignore_errors=True)
     if os.path.exists(CLIENT_SRC):
