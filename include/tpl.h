@@ -169,14 +169,22 @@ int tpl_permute_swizzled(const void *src, void *dst, int dtype_bytes, int rank,
                          const tpl_swizzle *dst_swizzle, hipStream_t stream);
 
 /*
- * Host-only planning, no device needed.  With TPL_GEOM_PAGES32 it runs the
- * pages' method on one warp region: shard, P = elements / 32, and the
- * smallest k whose XOR swizzle makes the read and the write phase
- * bank-conflict-free (declines with TPL_E_NO_K otherwise).  With
- * TPL_GEOM_GFX950 it returns the plan tpl_permute would launch (assuming
- * 256-byte aligned base pointers), with TPL_GEOM_GFX950_INPLACE the plan it
- * would launch with src == dst.  `out` is filled on every return.
- * elem_offsets may be NULL.
+ * Host-only planning, no device needed (permute_layout page, "Algorithm"
+ * steps 1 and 2: align the two layouts into one shard, then pick the XOR
+ * swizzle).  With TPL_GEOM_PAGES32 it runs the pages' method on one warp
+ * region: shard, P = elements / 32, and the smallest k whose XOR swizzle
+ * makes the read and the write phase bank-conflict-free (declines with
+ * TPL_E_NO_K otherwise).  With TPL_GEOM_GFX950 it returns the plan
+ * tpl_permute would launch (assuming 256-byte aligned base pointers), with
+ * TPL_GEOM_GFX950_INPLACE the plan it would launch with src == dst.
+ *
+ * Arguments are those of tpl_permute without the pointers and the stream.
+ * elem_offsets ({src, dst} in elements, NULL for {0, 0}) is taken because
+ * the device plan depends on it: the offsets set the alignment of both
+ * bases, which decides whether 16-byte vectors apply on each side.  `out`
+ * (caller-owned, may be NULL) is filled on every return, with out->status
+ * equal to the return value; on a non-OK return tpl_last_error() gives the
+ * reason.  Nothing is allocated or launched.
  */
 int tpl_plan(int dtype_bytes, int rank, const int64_t *extents,
              const int64_t *src_strides, const int64_t *dst_strides,
@@ -215,10 +223,23 @@ int tpl_permute_staged(const void *src, void *dst, int dtype_bytes, int rank,
                        int64_t batch, const tpl_swizzle *src_swizzle,
                        const tpl_swizzle *dst_swizzle, int xor_k, hipStream_t stream);
 
-/* Static text of a status code. */
+/*
+ * Static text of a status code, one phrase per reason the permute_layout
+ * page gives for declining a call ("What it accepts": dtype mismatch, extent
+ * mismatch, unsupported dtype byte width, layouts that do not slice or
+ * canonicalise, no conflict-free swizzle), plus this library's argument,
+ * aliasing and HIP errors.  Unknown codes give "unknown status".  The
+ * string is owned by the library and never freed.
+ */
 const char *tpl_status_string(int status);
 
-/* Reason text of this thread's last non-OK return (empty string if none). */
+/*
+ * Reason text of this thread's last non-OK return from any entry point
+ * (the status phrase of the page's "What it accepts" list, with the detail
+ * that failed), or an empty string if none.  The buffer is thread-local,
+ * owned by the library, and valid until the next failing call on the same
+ * thread.
+ */
 const char *tpl_last_error(void);
 
 #ifdef __cplusplus

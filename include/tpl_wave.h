@@ -2,12 +2,13 @@
  * tpl_wave.h -- the register-staged, XOR-swizzled permute of one lane group,
  * as a device function for HIP kernels on gfx950 (header only).
  *
- * permute_layout page, "Algorithm" step 3: each lane of a 32-lane group reads
- * its P elements through the source layout into registers, visiting
- * iteration j = r ^ ((lane >> shift) & mask) at unrolled step r, where the
- * iteration n = lane + 32 * j is decomposed row-major over the shard extent
- * and projected onto the side's strides; after a wave barrier the registers
- * are written back through the destination layout in the same order.  Both
+ * The per-lane program of the permute_layout page, "Algorithm" step 3.  At
+ * unrolled step r (0 <= r < P) a lane of a 32-lane group takes iteration
+ * j = r ^ ((lane >> shift) & mask); the linear index lane + 32 * j, split
+ * row-major over the shard extent and dotted with the source strides, gives
+ * the element it loads into register r.  Once every lane holds its P
+ * registers (a wave barrier), the same indices dotted with the destination
+ * strides give where each register is stored.  Both
  * operands normally live in LDS; src and dst may be the same buffer.  Either
  * side may be XOR-swizzled (an MMA-style LDS tile): its offsets then go
  * through swz(m) = m ^ ((m >> shift) & ymask) before the access.

@@ -2,12 +2,12 @@
 // (kernels_*.hip, one translation unit each), the plan cache and the C entry
 // points.
 //
-// permute_layout page, "Algorithm" step 3: each lane reads its elements
-// through the source layout into registers, the lanes synchronise, and the
-// registers are written back through the destination layout.  On gfx950 the
-// reads and writes go to HBM, so both sides are 16-byte vector accesses that
-// cover whole 128-byte lines, and the element exchange between them happens
-// in registers (lane quads, DPP) or through LDS with XOR-ordered phases.
+// The method is the register-staged exchange of the permute_layout page,
+// "Algorithm" step 3.  Here both ends are HBM: every kernel loads whole
+// 16-byte vectors along the source-contiguous mode, regroups elements across
+// lanes (DPP and permlane within lane quads, or an LDS tile whose two phases
+// use the XOR-ordered visiting order), and stores whole 16-byte vectors along
+// the destination-contiguous mode, so each side moves full 128-byte lines.
 // Data moves as integers only; no floating-point instruction touches it.
 #include <hip/hip_runtime.h>
 
