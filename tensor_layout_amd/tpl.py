@@ -21,7 +21,9 @@ from dataclasses import dataclass, field
 from typing import List, Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtpl.so")
+# TPL_LIBRARY names another build of the same library to load instead (the
+# tests' host-only sanitizer build uses it).
+LIB_PATH = os.environ.get("TPL_LIBRARY") or os.path.join(HERE, "libtpl.so")
 
 TPL_OK = 0
 TPL_E_ARG = 1
