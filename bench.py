@@ -167,6 +167,28 @@ def host_info():
     return {"cpu_model": model, "nproc": usable, "cpu_count": os.cpu_count()}
 
 
+def device_memory_props():
+    """HBM clock and bus width as the HIP runtime reports them
+    (hipDeviceGetAttribute, attributes hipDeviceAttributeMemoryClockRate = 60
+    and hipDeviceAttributeMemoryBusWidth = 59 of hip_runtime_api.h), and the
+    usual clock x width x 2 / 8 bandwidth formula on them.  On MI355X the
+    runtime reports 2 GHz and 8192 bits: the formula, which assumes two
+    transfers per pin per reported clock cycle, gives 4096 GB/s, half the
+    published 8 TB/s (8192 pins at 8 Gb/s).  The published figure stays the
+    peak."""
+    import ctypes
+    import torch
+    try:
+        lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        clk, bus = ctypes.c_int(), ctypes.c_int()
+        if lib.hipDeviceGetAttribute(ctypes.byref(clk), 60, 0) or lib.hipDeviceGetAttribute(ctypes.byref(bus), 59, 0):
+            return None
+    except OSError:
+        return None
+    return {"memory_clock_khz": clk.value, "memory_bus_width_bits": bus.value,
+            "clock_x_bus_x2_over_8_gbps": round(clk.value * 1e3 * bus.value * 2 / 8 / 1e9, 1)}
+
+
 def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
     """The oracle as it stands, single-threaded, on the full workload."""
     import numpy as np
@@ -258,7 +280,8 @@ def cpu_baseline_parallel(wl, x, y_ref, min_seconds=5.0, max_runs=200):
     }
 
 
-def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, do_ceiling=True):
+def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, do_ceiling=True,
+              cpu_seconds=(10.0, 5.0)):
     import numpy as np
     import torch
     from tensor_layout_amd import tpl
@@ -382,12 +405,13 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
             "kernel_ms_avg": round(avg_ms, 5),
             "host_enqueue_us": round(host_us, 2),
             "per_launch": per_launch,
+            "device_memory": device_memory_props(),
         },
     }
     ref = None
     if do_cpu:
-        out["cpu_baseline"], ref = cpu_baseline(wl, x)
-        out["cpu_baseline_parallel"] = cpu_baseline_parallel(wl, x, ref)
+        out["cpu_baseline"], ref = cpu_baseline(wl, x, min_seconds=cpu_seconds[0])
+        out["cpu_baseline_parallel"] = cpu_baseline_parallel(wl, x, ref, min_seconds=cpu_seconds[1])
     if do_verify:
         import oracle
         if ref is None:
@@ -479,10 +503,14 @@ def main():
     by_name = {w.name: w for w in workloads.ALL + workloads.INPLACE + [workloads.COPY_CALIBRATION]}
     if a.all:
         todo = workloads.ALL + workloads.INPLACE + ([workloads.COPY_CALIBRATION] if a.with_calibration else [])
+        # Every line carries the oracle's CPU throughput, on a shorter sample
+        # than the single-workload run (about 3 s single-threaded, 2 s on all
+        # host threads) so that the whole list stays within minutes.
+        cpu_s = (3.0, 2.0)
         if a.rounds <= 1:
             for wl in todo:
-                print(json.dumps(bench_one(wl, a.steps, a.warmup, False, not a.no_verify,
-                                           do_ceiling=not a.no_ceiling)), flush=True)
+                print(json.dumps(bench_one(wl, a.steps, a.warmup, not a.no_cpu, not a.no_verify,
+                                           do_ceiling=not a.no_ceiling, cpu_seconds=cpu_s)), flush=True)
             return
         # Rounds over all workloads in turn; the first round only warms the
         # machine up.  Outputs are checked in the last round.
@@ -490,8 +518,8 @@ def main():
         for r in range(a.rounds):
             last = r == a.rounds - 1
             for wl in todo:
-                out = bench_one(wl, a.steps, a.warmup, False, last and not a.no_verify,
-                                do_ceiling=last and not a.no_ceiling)
+                out = bench_one(wl, a.steps, a.warmup, last and not a.no_cpu, last and not a.no_verify,
+                                do_ceiling=last and not a.no_ceiling, cpu_seconds=cpu_s)
                 print(f"round {r + 1}/{a.rounds} {wl.name}: {out['roofline']['achieved']} GB/s",
                       file=sys.stderr, flush=True)
                 if r > 0:
@@ -500,7 +528,7 @@ def main():
             outs = sorted(kept[wl.name], key=lambda o: o["roofline"]["achieved"])
             med = dict(outs[len(outs) // 2])
             final = kept[wl.name][-1]
-            for key in ("bitexact",):
+            for key in ("bitexact", "cpu_baseline", "cpu_baseline_parallel"):
                 if key in final:
                     med[key] = final[key]
             roof = dict(med["roofline"])

@@ -53,6 +53,12 @@ SF_WORKED = Workload("sf_worked_example_2x1x4x32_f32", 4, (2, 1, 4, 32),
 SF_BATCHED = Workload("sf_transpose_2^20x4x32_f32", 4, (4, 32), (32, 1), (1, 4),
                       batch=1 << 20, seed=_seed(2), specials=True)
 
+# One GPU's share of the batched transpose when the batch is split over 8
+# GPUs: 2^17 tiles, 64 MiB each way (small enough for the Infinity Cache, so
+# the benchmark's buffer rotation keeps every launch cold).
+SF_SHARE_OF_8 = Workload("sf_transpose_2^17x4x32_f32", 4, (4, 32), (32, 1), (1, 4),
+                         batch=1 << 17, seed=_seed(2, 4), specials=True)
+
 # 65536 tiles of 128x64 fp16: row-major (64,1) -> column-major (1,128).
 TILE_128x64 = Workload("tile_65536x128x64_f16_rowmajor_to_colmajor", 2, (128, 64), (64, 1),
                        (1, 128), batch=65536, seed=_seed(3))
@@ -103,7 +109,7 @@ BF16_16K_INPLACE = Workload("transpose_16384x16384_bf16_inplace", 2, (16384, 163
 # size, used to calibrate the HBM byte counters.
 COPY_CALIBRATION = Workload("identity_copy_512MiB_u32", 4, (1 << 27,), (1,), (1,), seed=0x5EED0100)
 
-ALL = ([SF_WORKED, SF_BATCHED, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)]
+ALL = ([SF_WORKED, SF_BATCHED, SF_SHARE_OF_8, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)]
        + [BF16_16K, W16_4K, OUTER_PERM, SF_SWIZZLED, TILE_SWIZZLED, SF_U8, SF_F16, AOS_TO_SOA, AOS3_TO_SOA,
           BF16_16K_ODD_PITCH])
 INPLACE = [BF16_16K_INPLACE]

@@ -148,6 +148,7 @@ EXPECTED_KERNEL = {
     "axes0231_64x128x32x32_w8": "lds",
     "transpose_16384x16384_bf16": "lds",
     "transpose_4096x4096_16B": "lds",
+    "sf_transpose_2^17x4x32_f32": "quad",
     "axes1023_64x128x32x32_f32_runs": "copy",
     "sf_transpose_2^20x4x32_f32_to_swizzled": "quad",
     "tile_65536x128x64_f16_to_swizzled_colmajor": "lds",
