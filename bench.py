@@ -469,6 +469,40 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
     return out
 
 
+def launches_only(wl, k, entry="permute", xor_k=-1):
+    """K launches of one workload on uninitialised buffers, nothing timed or
+    checked: the run a rocprofv3 counter pass wraps (counters serialise the
+    kernels, and each workload's dispatches come out in this order)."""
+    import torch
+    from tensor_layout_amd import tpl
+    dev = torch.device("cuda:0")
+    ns, nd = buffer_bytes(wl)
+    if wl.inplace:
+        ns = nd = max(ns, nd)
+    # Fresh buffer pairs in turn, as many as the benchmark's rotation uses
+    # (up to K), so that small workloads stay out of the Infinity Cache too.
+    pairs = max(1, min(k, max(2, min(128, math.ceil(ROTATE_BYTES / (ns + nd))))))
+    srcs = [torch.empty(ns, dtype=torch.uint8, device=dev) for _ in range(pairs)]
+    dsts = srcs if wl.inplace else [torch.empty(nd, dtype=torch.uint8, device=dev) for _ in range(pairs)]
+    sp = torch.cuda.current_stream(dev).cuda_stream
+    prepared = tpl.PreparedPermute(wl.w, wl.extents, wl.src_strides, wl.dst_strides, wl.offsets, wl.batch,
+                                   wl.src_swizzle, wl.dst_swizzle)
+    for i in range(k):
+        src, dst = srcs[i % pairs], dsts[i % pairs]
+        if entry == "staged":
+            st = tpl.tpl_permute_staged(src.data_ptr(), dst.data_ptr(), wl.w, wl.extents, wl.src_strides,
+                                        wl.dst_strides, wl.offsets, wl.batch, xor_k, sp, wl.src_swizzle,
+                                        wl.dst_swizzle)
+        else:
+            st = prepared(src.data_ptr(), dst.data_ptr(), sp)
+        if st != tpl.TPL_OK:
+            raise tpl.TplError(st, tpl.tpl_last_error())
+    torch.cuda.synchronize()
+    print(f"launched {wl.name} x{k}", flush=True)
+    del srcs, dsts
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -480,7 +514,8 @@ def main():
                     help="with --all: run the workloads interleaved this many rounds, drop the first "
                          "round (when more than one) and report each workload's median round")
     ap.add_argument("--with-calibration", action="store_true",
-                    help="with --all: also run the 512 MiB identity copy used to scale HBM counters")
+                    help="with --all: also run identity copies of 8, 16, 32, 64 and 512 MiB (the 512 MiB "
+                         "one scales the HBM byte counters; all are same-size references)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
@@ -488,6 +523,9 @@ def main():
     ap.add_argument("--entry", choices=("permute", "staged"), default="permute",
                     help="tpl_permute (default) or the half-wave LDS-staged tpl_permute_staged")
     ap.add_argument("--xor-k", type=int, default=-1, help="staged entry: force this XOR k (-1 = planner's)")
+    ap.add_argument("--launches-only", type=int, default=0, metavar="K",
+                    help="K launches of the workload (or of every workload with --all, in list order) and "
+                         "nothing else: the program a rocprofv3 counter pass wraps")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the library has no multi-GPU path.",
@@ -500,9 +538,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    by_name = {w.name: w for w in workloads.ALL + workloads.INPLACE + [workloads.COPY_CALIBRATION]}
+    by_name = {w.name: w for w in workloads.ALL + workloads.INPLACE + workloads.COPY_REFERENCES}
+    if a.launches_only:
+        todo = (workloads.ALL + workloads.INPLACE + (workloads.COPY_REFERENCES if a.with_calibration else [])
+                if a.all else [by_name[a.workload]])
+        for wl in todo:
+            launches_only(wl, a.launches_only, a.entry, a.xor_k)
+        return
     if a.all:
-        todo = workloads.ALL + workloads.INPLACE + ([workloads.COPY_CALIBRATION] if a.with_calibration else [])
+        todo = workloads.ALL + workloads.INPLACE + (workloads.COPY_REFERENCES if a.with_calibration else [])
         # Every line carries the oracle's CPU throughput, on a shorter sample
         # than the single-workload run (about 3 s single-threaded, 2 s on all
         # host threads) so that the whole list stays within minutes.

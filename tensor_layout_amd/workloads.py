@@ -105,9 +105,12 @@ TILE_SWIZZLED = Workload("tile_65536x128x64_f16_to_swizzled_colmajor", 2, (128, 
 # The 16384^2 bf16 transpose with source and destination in one buffer.
 BF16_16K_INPLACE = Workload("transpose_16384x16384_bf16_inplace", 2, (16384, 16384), (16384, 1), (1, 16384),
                             seed=_seed(5, 2), inplace=True)
-# Not a workload of the method: an identity layout (a plain copy) of known
-# size, used to calibrate the HBM byte counters.
+# Not workloads of the method: identity layouts (plain copies) of known size,
+# used to calibrate the HBM byte counters (512 MiB) and as same-size copy
+# references for the counter profiles of the small permutes.
 COPY_CALIBRATION = Workload("identity_copy_512MiB_u32", 4, (1 << 27,), (1,), (1,), seed=0x5EED0100)
+COPY_REFERENCES = [Workload(f"identity_copy_{m}MiB_u32", 4, (m << 18,), (1,), (1,), seed=0x5EED0100 + m)
+                   for m in (8, 16, 32, 64)] + [COPY_CALIBRATION]
 
 ALL = ([SF_WORKED, SF_BATCHED, SF_SHARE_OF_8, TILE_128x64] + [mixed_width(w) for w in (1, 2, 4, 8)]
        + [BF16_16K, W16_4K, OUTER_PERM, SF_SWIZZLED, TILE_SWIZZLED, SF_U8, SF_F16, AOS_TO_SOA, AOS3_TO_SOA,
