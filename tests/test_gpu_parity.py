@@ -323,24 +323,40 @@ BIG_CASES = [
 ]
 
 
-def sampled_pairs(ext, ss, ds, batch, seed, count=4096):
-    """Source and destination element indices of `count` random coordinates, by the oracle's address rule."""
-    span_s = 1 + sum((e - 1) * s for e, s in zip(ext, ss))
-    span_d = 1 + sum((e - 1) * s for e, s in zip(ext, ds))
-    rng = np.random.default_rng(seed)
-    coords = np.stack([rng.integers(0, e, count) for e in ext], axis=1)
-    items = rng.integers(0, batch, count)
-    si = [int(b) * span_s + oracle.address(tuple(int(v) for v in c), ss) for b, c in zip(items, coords)]
-    di = [int(b) * span_d + oracle.address(tuple(int(v) for v in c), ds) for b, c in zip(items, coords)]
-    return si, di, span_s, span_d
+def oracle_threads(x, ref, w, ext, ss, ds, batch):
+    """The C oracle over the whole layout, run on slices of the outermost
+    index in host threads (the oracle's ctypes call releases the GIL).  By the
+    address rule, batch items [a, b) start a * span further on each side, and
+    with one item, rows [a, b) of the first mode start a * stride further."""
+    import concurrent.futures as cf
+    import os
+    span_s, span_d = cosize(ext, ss), cosize(ext, ds)
+    n = batch if batch > 1 else ext[0]
+    threads = max(1, min(16, os.cpu_count() or 1, n))
+    cuts = [n * i // threads for i in range(threads + 1)]
+
+    def one(a, b):
+        if batch > 1:
+            oracle.permute(x, ref, w, ext, ss, ds, (a * span_s, a * span_d), b - a)
+        else:
+            oracle.permute(x, ref, w, (b - a,) + tuple(ext[1:]), ss, ds, (a * ss[0], a * ds[0]), 1)
+
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda ab: one(*ab), [(a, b) for a, b in zip(cuts, cuts[1:]) if b > a]))
+    return ref
+
+
+def check_full(name, got, ref):
+    if not np.array_equal(got, ref):
+        diff = np.flatnonzero(got != ref)
+        raise AssertionError(f"{name}: {diff.size} bytes differ; first at byte {diff[0]}")
 
 
 @pytest.mark.parametrize("case", BIG_CASES, ids=lambda c: c[0])
-def test_big_index_paths_sampled(case):
-    """At least 2^31 elements (the kernels' 64-bit index instances): sampled
-    coordinates against the oracle's address rule, the whole result against
-    PyTorch's strided views of the same layouts, and no destination byte
-    left unwritten."""
+def test_big_index_paths(case):
+    """At least 2^31 elements (the kernels' 64-bit index instances): the whole
+    result against the oracle's, byte for byte, with the destination's
+    sentinel bytes on both sides."""
     torch = _torch()
     name, w, ext, ss, ds, batch, kernel = case
     n = batch
@@ -349,47 +365,41 @@ def test_big_index_paths_sampled(case):
     assert n >= 1 << 31
     plan = tpl.tpl_plan(w, ext, ss, ds, batch=batch)
     assert plan.kernel == kernel, plan
-    si, di, span_s, span_d = sampled_pairs(ext, ss, ds, batch, 11)
     print(f"\n[case] big index path {name}: {n} elements, kernel {plan.kernel}", flush=True)
+    nbs, nbd = batch * cosize(ext, ss) * w, batch * cosize(ext, ds) * w
     gen = torch.Generator("cuda").manual_seed(5)
-    x = torch.randint(0, 256, (batch * span_s,), dtype=torch.uint8, device="cuda", generator=gen)
-    d = torch.full((batch * span_d,), SENTINEL, dtype=torch.uint8, device="cuda")
+    x = torch.randint(0, 256, (nbs,), dtype=torch.uint8, device="cuda", generator=gen)
+    d = torch.full((nbd,), SENTINEL, dtype=torch.uint8, device="cuda")
     tpl.permute(d, x, ext, ss, ds, batch=batch, dtype_bytes=w)
     torch.cuda.synchronize()
-    xs = x[torch.tensor(si, device="cuda")].cpu().numpy()
-    ys = d[torch.tensor(di, device="cuda")].cpu().numpy()
-    assert np.array_equal(xs, ys)
-    bs, bd = (span_s,), (span_d,)
-    src_view = torch.as_strided(x, (batch,) + tuple(ext), bs + tuple(ss))
-    dst_view = torch.as_strided(d, (batch,) + tuple(ext), bd + tuple(ds))
-    assert torch.equal(src_view, dst_view)
-    # every destination element is covered by the layout, so a byte still
-    # holding the sentinel must hold it in the source too
-    assert int((d == SENTINEL).sum()) == int((src_view == SENTINEL).sum())
-    del x, d, src_view, dst_view
+    xh = x.cpu().numpy()
+    del x
+    got = d.cpu().numpy()
+    del d
     torch.cuda.empty_cache()
+    ref = oracle_threads(xh, np.full(nbd, SENTINEL, dtype=np.uint8), w, ext, ss, ds, batch)
+    check_full(name, got, ref)
 
 
-def test_big_in_place_transpose_sampled():
+def test_big_in_place_transpose():
     """A 65536 x 65536 byte matrix (2^32 elements) transposed in place by the
-    tile-pair swap kernel's 64-bit instance."""
+    tile-pair swap kernel's 64-bit instance, against the oracle's
+    out-of-place result on a copy of the input."""
     torch = _torch()
     ext, ss, ds = (65536, 65536), (65536, 1), (1, 65536)
     plan = tpl.tpl_plan(1, ext, ss, ds, geometry=tpl.TPL_GEOM_GFX950_INPLACE)
     assert plan.kernel == "swap", plan
-    si, di, _, _ = sampled_pairs(ext, ss, ds, 1, 13)
     print("\n[case] big in-place transpose 65536x65536 u8, kernel swap", flush=True)
     gen = torch.Generator("cuda").manual_seed(6)
     buf = torch.randint(0, 256, (1 << 32,), dtype=torch.uint8, device="cuda", generator=gen)
-    x0 = buf.clone()
+    x0 = buf.cpu().numpy()
     tpl.permute(buf, buf, ext, ss, ds, dtype_bytes=1)
     torch.cuda.synchronize()
-    xs = x0[torch.tensor(si, device="cuda")].cpu().numpy()
-    ys = buf[torch.tensor(di, device="cuda")].cpu().numpy()
-    assert np.array_equal(xs, ys)
-    assert torch.equal(buf.view(65536, 65536), x0.view(65536, 65536).t())
-    del buf, x0
+    got = buf.cpu().numpy()
+    del buf
     torch.cuda.empty_cache()
+    ref = oracle_threads(x0, np.full(1 << 32, SENTINEL, dtype=np.uint8), 1, ext, ss, ds, 1)
+    check_full("big in-place transpose", got, ref)
 
 
 # ---------------------------------------------------------------------------
@@ -494,26 +504,23 @@ def test_element_tiles_match_oracle(case):
              expect_kernel="etile", zs=zs, zd=zd)
 
 
-def test_element_tiles_full_size_sampled():
+def test_element_tiles_full_size():
     """A 16384 x 16384 bf16 transpose with source rows 16385 elements apart
-    (no 16-byte alignment on any row but the first): sampled coordinates
-    against the oracle's address rule and the whole result against strided
-    views."""
+    (no 16-byte alignment on any row but the first): the whole result
+    against the oracle's."""
     torch = _torch()
     ext, ss, ds = (16384, 16384), (16385, 1), (1, 16384)
     plan = tpl.tpl_plan(2, ext, ss, ds)
     assert plan.kernel == "etile", plan
-    si, di, span_s, span_d = sampled_pairs(ext, ss, ds, 1, 17)
     print("\n[case] element tiles 16384^2 bf16, source pitch 16385", flush=True)
+    nbs, nbd = cosize(ext, ss) * 2, cosize(ext, ds) * 2
     gen = torch.Generator("cuda").manual_seed(9)
-    x = torch.randint(0, 256, (span_s * 2,), dtype=torch.uint8, device="cuda", generator=gen).view(torch.int16)
-    d = torch.full((span_d * 2,), SENTINEL, dtype=torch.uint8, device="cuda").view(torch.int16)
+    x = torch.randint(0, 256, (nbs,), dtype=torch.uint8, device="cuda", generator=gen)
+    d = torch.full((nbd,), SENTINEL, dtype=torch.uint8, device="cuda")
     tpl.permute(d, x, ext, ss, ds, dtype_bytes=2)
     torch.cuda.synchronize()
-    xs = x[torch.tensor(si, device="cuda")].cpu().numpy()
-    ys = d[torch.tensor(di, device="cuda")].cpu().numpy()
-    assert np.array_equal(xs, ys)
-    assert torch.equal(torch.as_strided(x, ext, ss), torch.as_strided(d, ext, ds))
+    ref = oracle_threads(x.cpu().numpy(), np.full(nbd, SENTINEL, dtype=np.uint8), 2, ext, ss, ds, 1)
+    check_full("element tiles 16384^2", d.cpu().numpy(), ref)
 
 
 # ---------------------------------------------------------------------------
