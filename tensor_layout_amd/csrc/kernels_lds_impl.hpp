@@ -93,21 +93,25 @@ hipError_t launch_lds_width(const Plan& p, const LdsArgs& a, hipStream_t st) {
 #define TPL_LDS_SHAPE(W_, TB_, TA_, CPT_) \
     TPL_LDS_CASE(W_, TB_, TA_, CPT_, 16) TPL_LDS_CASE(W_, TB_, TA_, CPT_, 8) TPL_LDS_CASE(W_, TB_, TA_, CPT_, 4)
     if constexpr (W == 1) {
+        TPL_LDS_SHAPE(1, 128, 128, 4)
         TPL_LDS_SHAPE(1, 128, 128, 2)
         TPL_LDS_SHAPE(1, 64, 128, 2)
     }
     if constexpr (W == 2) {
+        TPL_LDS_SHAPE(2, 256, 64, 4)
         TPL_LDS_SHAPE(2, 256, 64, 2)
         TPL_LDS_SHAPE(2, 128, 128, 4)
         TPL_LDS_SHAPE(2, 128, 64, 2)
         TPL_LDS_SHAPE(2, 32, 64, 2)
     }
     if constexpr (W == 4) {
+        TPL_LDS_SHAPE(4, 128, 64, 4)
         TPL_LDS_SHAPE(4, 64, 64, 2)
         TPL_LDS_SHAPE(4, 32, 256, 2)
         TPL_LDS_SHAPE(4, 32, 32, 2)
     }
     if constexpr (W == 8) {
+        TPL_LDS_SHAPE(8, 64, 64, 4)
         TPL_LDS_SHAPE(8, 32, 64, 2)
         TPL_LDS_SHAPE(8, 16, 32, 2)
     }

@@ -374,6 +374,24 @@ static const LdsShape kLdsShortDst[] = {
     {4, 32, 256, 2},
 };
 
+// Shapes for transposes whose tiles are strided on both sides (each tile
+// reads and writes row pieces of a larger matrix), one per width: 32 KiB
+// tiles of 512 threads (16 KiB for 16-byte elements), with dynamic LDS
+// reserved so that at most two workgroups share a CU (kTwoPerCuLds: more
+// than a third, at most half of the 160 KiB).  Fewer tiles in flight per CU
+// relieve the L2 crossbar and the DRAM credit stalls that bound these
+// layouts.  Measured on MI355X against the same transposes with the shapes
+// below and up to four workgroups per CU: bf16 16384^2 176 us (was 185),
+// fp32 8192^2 89.5 us (95.0), u64 4096^2 43.9 us (48.4), u8 16384^2
+// 96.0 us (98.3), 16-byte 4096^2 90.5 us (92.2); never slower down to
+// 32 MiB each way.  Tiles whose footprint is one contiguous block on a side
+// (whole rows of adjacent destination rows) measured slower with the cap,
+// and keep the shapes below.
+static const LdsShape kLdsStrided[] = {
+    {1, 128, 128, 4}, {2, 256, 64, 4}, {4, 128, 64, 4}, {8, 64, 64, 4}, {16, 64, 16, 2},
+};
+static constexpr int kTwoPerCuLds = 55 * 1024;
+
 static std::mutex g_choice_mu;
 
 static LdsChoice cached_choice(const LdsShape& sh) {
@@ -671,12 +689,26 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
         // Tiled LDS transpose.
         if (vec16 && ma.e * w >= 64 && mb.e * w >= 64 && src_ok && dst_ok) {
             const LdsShape* pick = nullptr;
+            bool two_per_cu = false;
             if (ma.e >= 4 * mb.e) {
                 for (const LdsShape& s : kLdsShortDst)
                     if (s.w == w && s.tb <= mb.e && s.ta <= ma.e) {
                         pick = &s;
                         break;
                     }
+            } else {
+                for (const LdsShape& s : kLdsStrided) {
+                    if (s.w != w || s.tb > mb.e || s.ta > ma.e) continue;
+                    // a tile's destination (source) footprint is one block when
+                    // it spans whole destination (source) rows that are adjacent
+                    const bool dst_block = s.tb == mb.e && ma.d == mb.e;
+                    const bool src_block = s.ta == ma.e && mb.s == ma.e;
+                    if (!dst_block && !src_block) {
+                        pick = &s;
+                        two_per_cu = true;
+                    }
+                    break;
+                }
             }
             for (const LdsShape& s : kLdsShapes) {
                 if (pick) break;
@@ -731,6 +763,7 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             p.block = pick->threads();
             p.grid = l.ntiles;
             p.lds_bytes = pick->tb * c.pitch;
+            if (two_per_cu && p.lds_bytes < kTwoPerCuLds) p.lds_bytes = kTwoPerCuLds;
             p.unit_is_item = (l.ntb == 1 && l.nta == 1 && mb.e == pick->tb && ma.e == pick->ta);
             return p;
         }

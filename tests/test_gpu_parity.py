@@ -553,35 +553,49 @@ def test_rank8_permutations_match_oracle(case):
 # ---------------------------------------------------------------------------
 # Every tile shape the tiled transpose instantiates, picked by extents just
 # past the shape (ragged edges on both modes), as one item and as two items
-# of a batch mode.  The short-destination shapes are picked when the
-# source-contiguous extent is at least four times the destination-contiguous
-# one, so their cases take a long source-contiguous mode.
+# of a batch mode.  Shapes carry their chunks per thread; how a case reaches
+# its shape:
+#   strided    -- the width's 32 KiB shape run at two workgroups per CU (tiles
+#                 strided on both sides, source rows shorter than 4x the
+#                 destination's);
+#   short_dst  -- the source-contiguous extent at least 4x the destination-
+#                 contiguous one;
+#   dst_block  -- destination rows of exactly the tile's extent, adjacent, so a
+#                 tile's destination is one block and the general list applies;
+#   general    -- extents too small for the strided shape.
 
-LDS_SHAPES = [(1, 128, 128), (1, 64, 128), (2, 256, 64), (2, 128, 64), (2, 32, 64), (4, 64, 64), (4, 32, 32),
-              (8, 32, 64), (8, 16, 32), (16, 64, 16), (16, 16, 64), (16, 16, 16),
-              (2, 128, 128, "short_dst"), (4, 32, 256, "short_dst")]
+LDS_SHAPES = [
+    (1, 128, 128, 4, "strided"), (1, 128, 128, 2, "dst_block"), (1, 64, 128, 2, "general"),
+    (2, 256, 64, 4, "strided"), (2, 256, 64, 2, "dst_block"), (2, 128, 64, 2, "general"), (2, 32, 64, 2, "general"),
+    (2, 128, 128, 4, "short_dst"),
+    (4, 128, 64, 4, "strided"), (4, 64, 64, 2, "general"), (4, 32, 32, 2, "general"), (4, 32, 256, 2, "short_dst"),
+    (8, 64, 64, 4, "strided"), (8, 32, 64, 2, "general"), (8, 16, 32, 2, "general"),
+    (16, 64, 16, 2, "strided"), (16, 64, 16, 2, "dst_block"), (16, 16, 64, 2, "general"), (16, 16, 16, 2, "general"),
+]
 
 
-def _shape_case(w, tb, ta, short_dst=False):
+def _shape_case(w, tb, ta, mode):
     eb, ea = tb + 3, ta + 5
-    if short_dst:
+    if mode == "short_dst":
         ea = max(ea, 4 * eb)
+    if mode == "dst_block":
+        eb = tb
     pa = -(-ea * w // 16) * 16 // w    # rows padded to whole 16-byte chunks
-    pb = -(-eb * w // 16) * 16 // w
+    pb = eb if mode == "dst_block" else -(-eb * w // 16) * 16 // w
     return eb, ea, pa, pb
 
 
-@pytest.mark.parametrize("shape", LDS_SHAPES, ids=lambda s: f"w{s[0]}_{s[1]}x{s[2]}" + ("_short_dst" if len(s) > 3 else ""))
+@pytest.mark.parametrize("shape", LDS_SHAPES, ids=lambda s: f"w{s[0]}_{s[1]}x{s[2]}_cpt{s[3]}_{s[4]}")
 def test_every_lds_tile_shape(shape):
-    w, tb, ta = shape[:3]
-    eb, ea, pa, pb = _shape_case(w, tb, ta, len(shape) > 3)
+    w, tb, ta, cpt, mode = shape
+    eb, ea, pa, pb = _shape_case(w, tb, ta, mode)
     ext, ss, ds = (eb, ea), (pa, 1), (1, pb)
     p = tpl.tpl_plan(w, ext, ss, ds)
-    assert p.kernel == "lds" and tuple(p.tile) == (tb, ta), p
-    run_case(f"lds_shape_w{w}_{tb}x{ta}", w, ext, ss, ds, seed=tb * 7 + ta)
+    assert p.kernel == "lds" and tuple(p.tile) == (tb, ta) and p.chunks_per_thread == cpt, p
+    run_case(f"lds_shape_w{w}_{tb}x{ta}_cpt{cpt}_{mode}", w, ext, ss, ds, seed=tb * 7 + ta + cpt)
     # two items 16-byte aligned apart: one batch mode
     item_s, item_d = eb * pa + 16 // min(w, 16), ea * pb + 16 // min(w, 16)
     ext3, ss3, ds3 = (2, eb, ea), (item_s, pa, 1), (item_d, 1, pb)
     p3 = tpl.tpl_plan(w, ext3, ss3, ds3)
-    assert p3.kernel == "lds" and tuple(p3.tile) == (tb, ta), p3
-    run_case(f"lds_shape_w{w}_{tb}x{ta}_two_items", w, ext3, ss3, ds3, seed=tb * 7 + ta + 1)
+    assert p3.kernel == "lds" and tuple(p3.tile) == (tb, ta) and p3.chunks_per_thread == cpt, p3
+    run_case(f"lds_shape_w{w}_{tb}x{ta}_cpt{cpt}_{mode}_two_items", w, ext3, ss3, ds3, seed=tb * 7 + ta + cpt + 1)
