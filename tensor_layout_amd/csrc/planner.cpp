@@ -391,6 +391,7 @@ static const LdsShape kLdsStrided[] = {
     {1, 128, 128, 4}, {2, 256, 64, 4}, {4, 128, 64, 4}, {8, 64, 64, 4}, {16, 64, 16, 2},
 };
 static constexpr int kTwoPerCuLds = 55 * 1024;
+static constexpr int kThreePerCuLds = 41 * 1024;
 
 static std::mutex g_choice_mu;
 
@@ -1051,6 +1052,13 @@ Plan plan_inplace(int w, int rank, const int64_t* ext, const int64_t* ss, const 
     p.block = pick->threads();
     p.grid = l.ntiles;
     p.lds_bytes = 2 * T * c.pitch;
+    // Long launches run at most three pair-swap workgroups per CU (reserved
+    // LDS: more than a quarter, at most a third of the 160 KiB): on the
+    // 16384^2 bf16 transpose in place (34816 workgroups of 256 lanes) 191 us
+    // against 200.6 us with up to eight per CU; four per CU measured 191.7,
+    // five 199.3.  Below 8 rounds of three per CU on 256 CUs the cap would
+    // only lengthen the launch's tail, so it applies from 6144 workgroups.
+    if (p.grid >= 6144 && p.lds_bytes < kThreePerCuLds) p.lds_bytes = kThreePerCuLds;
     p.unit_is_item = false;
     return p;
 }
