@@ -91,7 +91,7 @@ __device__ __forceinline__ void etile_loop(const LdsArgs& a, uint8_t* lds) {
 // item's first and last rows.  SHIFT = false compiles the case where every
 // destination row is on 16 bytes (delta = 0, TB rows) without the shift
 // arithmetic.
-template <int W, int NB, bool BIG, bool SHIFT>
+template <int W, int NB, bool BIG, bool SHIFT, int G>
 __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
     typedef typename Elem<W>::type T;
     constexpr EtileShape ES = kEtileShapes[etile_index(W)];
@@ -102,7 +102,7 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
     constexpr int L = 128 / ES.g;                       // lanes per LDS write pass
     constexpr int XR = E - 1;                           // rows loaded past TB for shifted columns
     static_assert(NT % QS == 0 && NT % QD == 0 && TB % RS == 0 && TA % CS == 0 && TB <= NT && TA <= NT &&
-                      TB % L == 0 && XR * (QS + 1) <= NT,
+                      TB % L == 0 && XR * (QS + 1) <= NT && ND % G == 0,
                   "tile must tile the threads");
     static_assert(ES.rp >= (QS + 1) * 16 && ES.vrow(1) % ES.g == 0 && ES.rp % ES.g == 0 && ES.sk % ES.g == 0,
                   "LDS rows must hold every chunk at the write piece's alignment");
@@ -147,87 +147,90 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
             }
         };
         {
-            u32x4 v[NS + 1];
-            int at_lds[NS + 1];
-            bool on[NS + 1];
+            // Every lane loads and writes to LDS in each of the NS steps: a lane
+            // whose chunk lies past its row piece or whose row lies past the
+            // item loads the tile's first chunk instead and writes it to its
+            // own slot, bytes that phase 2 never reads.  With the writes
+            // unconditional no load is left outstanding on any path through
+            // the loop, and the compiler issues the NS loads back to back;
+            // conditional writes made it wait for each load before issuing
+            // the next (16384^2 bf16, source pitch 16385: 212 -> 206 us).
+            u32x4 v[NS];
+            int at_lds[NS];
+            const uint8_t* first = s0 - L0;
 #pragma unroll
-            for (int i = 0; i <= NS; ++i) {
-                // steps: NS of whole row pieces, then the extra chunks of rows < TB
-                const int bb = i < NS ? r1 + i * RS : t / L + (TB / L) * (t % L);
-                const int q = i < NS ? q1 : QS;
+            for (int i = 0; i < NS; ++i) {
+                const int bb = r1 + i * RS;
                 const int lead = (int)((L0 + (uint32_t)bb * pm) & 15);
-                on[i] = (i < NS || t < TB) && bb < nl && q * 16 < lead + na * W;
-                at_lds[i] = ES.vrow(bb) + q * 16;
-                if (on[i]) {
-                    // The first and last chunk of a row piece may hold bytes
-                    // of the neighbouring tiles' pieces: ordinary loads keep
-                    // them in L2 for those tiles (non-temporal ones let the
-                    // 16384^2 bf16 transpose with pitch 16385 fetch 1.8x).
-                    const uint8_t* g = s0 + bb * srow - lead + q * 16;
-                    if (q == 0 || q * 16 + 16 > lead + na * W) v[i] = *reinterpret_cast<const u32x4*>(g);
-                    else v[i] = ld16(g);
-                }
+                const bool on = bb < nl && q1 * 16 < lead + na * W;
+                at_lds[i] = ES.vrow(bb) + q1 * 16;
+                const uint8_t* g = on ? s0 + bb * srow - lead + q1 * 16 : first;
+                // The first and last chunk of a row piece may hold bytes of
+                // the neighbouring tiles' pieces: ordinary loads keep them in
+                // L2 for those tiles (non-temporal ones let the 16384^2 bf16
+                // transpose with pitch 16385 fetch 1.8x).
+                if (q1 == 0 || q1 * 16 + 16 > lead + na * W) v[i] = *reinterpret_cast<const u32x4*>(g);
+                else v[i] = ld16(g);
+            }
+            if (t < TB) {
+                // the extra chunk of a row piece not starting on 16 bytes
+                const int bb = t / L + (TB / L) * (t % L);
+                const int lead = (int)((L0 + (uint32_t)bb * pm) & 15);
+                if (bb < nl && QS * 16 < lead + na * W)
+                    put(ES.vrow(bb) + QS * 16, QS, *reinterpret_cast<const u32x4*>(s0 + bb * srow - lead + QS * 16));
+            }
+            if (shifted && t < XR * (QS + 1)) {
+                // rows TB.. of shifted columns: thread t takes chunk t % (QS + 1) of
+                // row TB + t / (QS + 1); the next tile reads them too (ordinary loads)
+                const int bb = TB + t / (QS + 1), q = t % (QS + 1);
+                const int lead = (int)((L0 + (uint32_t)bb * pm) & 15);
+                if (bb < nl && q * 16 < lead + na * W)
+                    put(ES.vrow(bb) + q * 16, q, *reinterpret_cast<const u32x4*>(s0 + bb * srow - lead + q * 16));
             }
 #pragma unroll
-            for (int i = 0; i <= NS; ++i) {
-                if (on[i]) put(at_lds[i], i < NS ? q1 : QS, v[i]);
-            }
-        }
-        if (shifted && t < XR * (QS + 1)) {
-            // rows TB.. of shifted columns: thread t takes chunk t % (QS + 1) of
-            // row TB + t / (QS + 1); the next tile reads them too (ordinary loads)
-            const int bb = TB + t / (QS + 1), q = t % (QS + 1);
-            const int lead = (int)((L0 + (uint32_t)bb * pm) & 15);
-            if (bb < nl && q * 16 < lead + na * W)
-                put(ES.vrow(bb) + q * 16, q, *reinterpret_cast<const u32x4*>(s0 + bb * srow - lead + q * 16));
+            for (int i = 0; i < NS; ++i) put(at_lds[i], q1, v[i]);
         }
         __syncthreads();
         {
             uint8_t* d0 = a.dst + (d_o + a0 * a.d_a + b0) * W;   // the tile's destination row 0
             const int64_t drow = a.d_a * W;
             const int rows = (int)(a.e_b - b0 < TB + XR ? a.e_b - b0 : TB + XR);   // of the item, from b0
-#pragma unroll
-            for (int i = 0; i <= ND; ++i) {
-                const int aa = i < ND ? c2 + i * CS : t;
-                if (!((i < ND || t < TA) && aa < na)) continue;
-                uint8_t* D = d0 + aa * drow;
-                int rel, lo, hi;                   // chunk start (bytes from D) and the rows [lo, hi) stored
+            union Chunk {
+                u32x4 v;
+                T e[E];
+            };
+            // The rows [lo, hi) a column stores and its chunk's start (bytes from
+            // its destination row at b0).
+            auto span = [&](int aa, int& rel, int& lo, int& hi) {
                 if constexpr (SHIFT) {
-                    const int lead = (int)((uint32_t)(uintptr_t)D & 15);
+                    const int lead = (int)((uint32_t)(uintptr_t)(d0 + aa * drow) & 15);
                     const int dw = (16 - lead) & 15;   // bytes to the next 16-byte boundary: delta W
-                    if (i < ND) {
-                        rel = dw + q2 * 16;
-                        lo = dw / W;
-                        hi = lo + TB < rows ? lo + TB : rows;
-                    } else {
-                        if (tbi != 0 || lead == 0) continue;   // the item's first rows [0, delta)
-                        rel = -lead;
-                        lo = 0;
-                        hi = dw / W < rows ? dw / W : rows;
-                    }
+                    rel = dw + q2 * 16;
+                    lo = dw / W;
+                    hi = lo + TB < rows ? lo + TB : rows;
                 } else {
-                    if (i == ND) continue;
                     rel = q2 * 16;
                     lo = 0;
                     hi = nb;
                 }
-                if (rel >= hi * W) continue;
-                const int bbf = rel / W;           // exact: lead is a multiple of W
-                union {
-                    u32x4 v;
-                    T e[E];
-                } u;
+            };
+            // Element (bb, aa) sits at its row's lead; rows outside [lo, hi)
+            // read row lo (a partial chunk stores no such element).
+            auto gather = [&](int aa, int rel, int lo, int hi, Chunk& u) {
+                const int bbf = rel / W;   // exact: lead is a multiple of W
 #pragma unroll
                 for (int j = 0; j < E; ++j) {
-                    // rows not stored read row lo (a partial chunk stores no such element)
                     const int bb = (unsigned)(bbf + j - lo) < (unsigned)(hi - lo) ? bbf + j : lo;
                     const int ls = (int)((L0 + (uint32_t)bb * pm) & 15);
                     u.e[j] = *reinterpret_cast<const T*>(lds + ES.vrow(bb) + ls + aa * W);
                 }
+            };
+            auto emit = [&](uint8_t* D, int rel, int lo, int hi, const Chunk& u) {
                 if (rel >= lo * W && rel + 16 <= hi * W) {
                     st16(D + rel, u.v);
                 } else {
                     // A chunk the row piece covers in part: its elements one by one.
+                    const int bbf = rel / W;
 #pragma unroll
                     for (int j = 0; j < E; ++j) {
                         // Ordinary stores: the chunk's other bytes may come
@@ -237,25 +240,71 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
                             *reinterpret_cast<T*>(D + rel + j * W) = u.e[j];
                     }
                 }
+            };
+            // The LDS reads of G steps first, then their stores: columns past
+            // the item read in-bounds LDS bytes and store nothing.
+#pragma unroll
+            for (int i0 = 0; i0 < ND; i0 += G) {
+                Chunk u[G];
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    int rel, lo, hi;
+                    span(c2 + (i0 + i) * CS, rel, lo, hi);
+                    gather(c2 + (i0 + i) * CS, rel, lo, hi, u[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const int aa = c2 + (i0 + i) * CS;
+                    int rel, lo, hi;
+                    span(aa, rel, lo, hi);
+                    if (aa < na && rel < hi * W) emit(d0 + aa * drow, rel, lo, hi, u[i]);
+                }
+            }
+            if constexpr (SHIFT) {
+                // The item's first tile also stores rows [0, delta) of each
+                // column whose destination row is not on 16 bytes (thread t:
+                // column t).
+                if (t < TA && t < na && tbi == 0) {
+                    uint8_t* D = d0 + t * drow;
+                    const int lead = (int)((uint32_t)(uintptr_t)D & 15);
+                    const int dw = (16 - lead) & 15;
+                    const int hi = dw / W < rows ? dw / W : rows;
+                    if (lead != 0 && -lead < hi * W) {
+                        Chunk c;
+                        gather(t, -lead, 0, hi, c);
+                        emit(D, -lead, 0, hi, c);
+                    }
+                }
             }
         }
         __syncthreads();   // LDS is reused by the next tile of this workgroup
     }
 }
 
+// Destination steps of the vector form whose LDS reads are issued together,
+// before their stores: all of them, but one at a time for 1-byte elements in
+// the shifted form, where each element holds a register until packed (all
+// four steps took 178 VGPRs and ran 6 % slower than the one-step form on
+// u8 16384^2 with destination pitch 16387; two steps 1 % slower).
+template <int W, bool SHIFT>
+constexpr int etile_read_group() {
+    constexpr EtileShape ES = kEtileShapes[etile_index(W)];
+    constexpr int ND = ES.ta / (256 / (ES.tb * W / 16));
+    return W == 1 && SHIFT ? 1 : ND;
+}
+
 // The two forms are separate kernels: the element form's swizzle branch
 // would otherwise set the vector form's register count.
-template <int W, int NB, bool BIG, bool SHIFT>
+template <int W, int NB, bool BIG, bool SHIFT, int G_ = etile_read_group<W, SHIFT>()>
 __global__ void __launch_bounds__(256) k_etile_vec(LdsArgs a) {
-    constexpr EtileShape ES = kEtileShapes[etile_index(W)];
-    __shared__ __attribute__((aligned(16))) uint8_t lds[SHIFT ? ES.vbytes() : ES.vrow(ES.tb)];
-    etile_vec_loop<W, NB, BIG, SHIFT>(a, lds);
+    // the plan's LDS bytes: vrow(TB) (vrow(TB + 16 / W - 1) shifted) or more
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    etile_vec_loop<W, NB, BIG, SHIFT, G_>(a, lds);
 }
 
 template <int W, int NB, bool BIG>
 __global__ void __launch_bounds__(256) k_etile(LdsArgs a) {
-    constexpr EtileShape ES = kEtileShapes[etile_index(W)];
-    __shared__ __attribute__((aligned(16))) uint8_t lds[ES.tb * ES.pitch()];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];   // TB x pitch bytes
     // Plain operands take the code without swizzle arithmetic (a uniform branch).
     if ((a.zs.ymask | a.zd.ymask) == 0) etile_loop<W, NB, BIG, false>(a, lds);
     else etile_loop<W, NB, BIG, true>(a, lds);
@@ -273,16 +322,16 @@ hipError_t launch_etile(const Plan& p, const uint8_t* src, uint8_t* dst, hipStre
     dim3 grid((unsigned)cap_grid(p.grid, 256)), block(256);
 #define TPL_ETILE_CASE(W_)                                                                   \
     case W_:                                                                                 \
-        if (a.vform == 1) hipLaunchKernelGGL((k_etile_vec<W_, NB, BIG, false>), grid, block, 0, st, a); \
-        else if (a.vform == 2) hipLaunchKernelGGL((k_etile_vec<W_, NB, BIG, true>), grid, block, 0, st, a); \
-        else hipLaunchKernelGGL((k_etile<W_, NB, BIG>), grid, block, 0, st, a);              \
+        if (a.vform == 1) hipLaunchKernelGGL((k_etile_vec<W_, NB, BIG, false>), grid, block, p.lds_bytes, st, a); \
+        else if (a.vform == 2) hipLaunchKernelGGL((k_etile_vec<W_, NB, BIG, true>), grid, block, p.lds_bytes, st, a); \
+        else hipLaunchKernelGGL((k_etile<W_, NB, BIG>), grid, block, p.lds_bytes, st, a);              \
         break;
     switch (p.w) {
         TPL_ETILE_CASE(1)
         TPL_ETILE_CASE(2)
         TPL_ETILE_CASE(4)
-    case 8: hipLaunchKernelGGL((k_etile<8, NB, BIG>), grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_etile<16, NB, BIG>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_etile<8, NB, BIG>), grid, block, p.lds_bytes, st, a); break;
+    default: hipLaunchKernelGGL((k_etile<16, NB, BIG>), grid, block, p.lds_bytes, st, a); break;
     }
 #undef TPL_ETILE_CASE
     return hipGetLastError();

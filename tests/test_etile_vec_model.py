@@ -12,7 +12,11 @@ description, not shared with it:
   na w are read whole and written to LDS at vrow(bb) + 16 q, where vrow(bb) =
   bb rp + sk (bb >> le); thread t takes chunk t % QS of rows t / QS + i RS,
   then thread t < TB the extra chunk QS of row t / L + (TB / L) (t % L), L =
-  128 / g being the lanes of one LDS write pass;
+  128 / g being the lanes of one LDS write pass; in the first NS steps a
+  lane whose row lies past the item or whose chunk lies past its row piece
+  loads the tile's first chunk and writes it to its own slot, so that every
+  lane writes in every step; no slot is written twice, and phase 2 reads
+  none of those bytes;
 * storing: tile column aa owns destination rows [delta, delta + TB) (from
   b0; clipped to the item), delta = the elements from its destination row's
   address at b0 to the next 16-byte boundary, so that its chunks are whole;
@@ -82,23 +86,33 @@ def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
             nl = min(TB + E - 1, e_b - b0) if shifted else nb   # rows loaded
             lds = np.full(lds_bytes, 0xEE, dtype=np.uint8)
             written = np.zeros(lds_bytes, dtype=bool)
+            junk = np.zeros(lds_bytes, dtype=bool)   # slots written with bytes never read
             lead_s = {}
             # phase 1
+            row0 = (so + b0 * s_b + a0) * w
+            first = row0 - row0 % 16                         # the tile's first chunk
             for t in range(NT):
-                slots = [(t // QS + i * RS, t % QS) for i in range(TB // RS)]
+                main = [(t // QS + i * RS, t % QS) for i in range(TB // RS)]
+                slots = list(main)
                 if t < TB:
                     L = 128 // g
                     slots.append((t // L + (TB // L) * (t % L), QS))
-                if t < (E - 1) * (QS + 1):
+                if shifted and t < (E - 1) * (QS + 1):
                     slots.append((TB + t // (QS + 1), t % (QS + 1)))
                 for bb, q in slots:
-                    if bb >= nl:
-                        continue
                     row = (so + (b0 + bb) * s_b + a0) * w   # byte offset in the source buffer
                     lead = row % 16                          # buffer base is 16-byte aligned
-                    lead_s[bb] = lead
-                    if q * 16 >= lead + na * w:
+                    if bb >= nl or q * 16 >= lead + na * w:
+                        if (bb, q) in main:
+                            # a main-step lane with nothing to load loads the
+                            # tile's first chunk and writes it to its own slot
+                            chunks.append(first)
+                            l = vrow(bb, rp, sk, le) + 16 * q
+                            assert 0 <= l and l + 16 <= vrow(bb + 1, rp, sk, le) and l + 16 <= lds_bytes
+                            assert not written[l:l + 16].any() and not junk[l:l + 16].any()
+                            junk[l:l + 16] = True
                         continue
+                    lead_s[bb] = lead
                     A = row - lead + 16 * q
                     assert A % 16 == 0
                     # the chunk holds at least one byte of this row piece
@@ -107,7 +121,7 @@ def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
                     l = vrow(bb, rp, sk, le) + 16 * q
                     assert l % g == 0 and 0 <= l and l + 16 <= lds_bytes
                     assert l + 16 <= vrow(bb + 1, rp, sk, le)   # stays in its own row
-                    assert not written[l:l + 16].any()
+                    assert not written[l:l + 16].any() and not junk[l:l + 16].any()
                     written[l:l + 16] = True
                     lds[l:l + 16] = xs[16 + A:16 + A + 16]
             # phase 2
@@ -116,6 +130,19 @@ def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
                 if t < TA:
                     slots.append((t, QD))
                 for aa, q in slots:
+                    if q < QD:
+                        # the kernel reads the LDS bytes of every main-step
+                        # slot before its stores, columns past the item
+                        # included: rows outside [lo, hi) read row lo
+                        Dx = (d_o + (a0 + aa) * d_a + b0) * w
+                        dl = (16 - Dx % 16) % 16 if shifted else 0
+                        lo_x = dl // w
+                        hi_x = min(lo_x + TB, e_b - b0)
+                        for j in range(16 // w):
+                            bx = (dl + 16 * q) // w + j
+                            bx = bx if lo_x <= bx < hi_x else lo_x
+                            lx = vrow(bx, rp, sk, le) + (row0 + bx * s_b * w) % 16 + aa * w
+                            assert 0 <= lx and lx + w <= min(lds_bytes, vrow(bx, rp, sk, le) + rp), (aa, q, bx)
                     if aa >= na:
                         continue
                     D = (d_o + (a0 + aa) * d_a + b0) * w
