@@ -33,7 +33,10 @@ __device__ __forceinline__ void etile_loop(const LdsArgs& a, uint8_t* lds) {
     constexpr EtileShape ES = kEtileShapes[etile_index(W)];
     constexpr int TB = ES.tb, TA = ES.ta, P = ES.pitch(), NT = 256;
     constexpr int RA = NT / TA, RB = NT / TB;   // rows per step, phase 1 and 2
-    static_assert(NT % TA == 0 && NT % TB == 0 && TB % RA == 0 && TA % RB == 0, "tile must tile the threads");
+    constexpr int U1 = TB / RA < 16 ? TB / RA : 16, U2 = TA / RB < 16 ? TA / RB : 16;   // steps per batch
+    static_assert(NT % TA == 0 && NT % TB == 0 && TB % RA == 0 && TA % RB == 0 && (TB / RA) % U1 == 0 &&
+                      (TA / RB) % U2 == 0,
+                  "tile must tile the threads");
     const int t = threadIdx.x;
     const int aa1 = t % TA, bb1 = t / TA;   // phase 1: column aa1, rows bb1 + i RA
     const int bb2 = t % TB, aa2 = t / TB;   // phase 2: column bb2, rows aa2 + i RB
@@ -47,26 +50,48 @@ __device__ __forceinline__ void etile_loop(const LdsArgs& a, uint8_t* lds) {
         const int64_t b0 = tbi * TB, a0 = tai * TA;
         const int nb = (int)(a.e_b - b0 < TB ? a.e_b - b0 : TB), na = (int)(a.e_a - a0 < TA ? a.e_a - a0 : TA);
         {
+            // U steps at a time: U loads back to back, then their LDS writes.
+            // A lane outside the item loads the tile's first element and
+            // writes it to its own slot, which phase 2 never reads: with
+            // unconditional writes no load stays outstanding on any path, so
+            // the loads need not wait for one another.
+            const int64_t first = (so + b0 * a.s_b + a0) * W;
             int64_t off = (so + (b0 + bb1) * a.s_b + a0 + aa1) * W;
             const int64_t step = (int64_t)RA * a.s_b * W;
-#pragma unroll 16
-            for (int i = 0; i < TB / RA; ++i, off += step) {
-                const int bb = bb1 + i * RA;
-                if (aa1 < na && bb < nb)
-                    *reinterpret_cast<T*>(lds + bb * P + aa1 * W) =
-                        __builtin_nontemporal_load(reinterpret_cast<const T*>(at<SWZ>(a.src, off, a.zs)));
+#pragma unroll
+            for (int i0 = 0; i0 < TB / RA; i0 += U1) {
+                T v[U1];
+#pragma unroll
+                for (int u = 0; u < U1; ++u) {
+                    const int bb = bb1 + (i0 + u) * RA;
+                    const bool on = aa1 < na && bb < nb;
+                    v[u] = __builtin_nontemporal_load(
+                        reinterpret_cast<const T*>(at<SWZ>(a.src, on ? off + u * step : first, a.zs)));
+                }
+#pragma unroll
+                for (int u = 0; u < U1; ++u)
+                    *reinterpret_cast<T*>(lds + (bb1 + (i0 + u) * RA) * P + aa1 * W) = v[u];
+                off += U1 * step;
             }
         }
         __syncthreads();
         {
+            // U steps at a time: the LDS reads (in bounds for every lane), then
+            // the stores of the elements inside the item.
             int64_t off = (d_o + (a0 + aa2) * a.d_a + b0 + bb2) * W;
             const int64_t step = (int64_t)RB * a.d_a * W;
-#pragma unroll 16
-            for (int i = 0; i < TA / RB; ++i, off += step) {
-                const int aa = aa2 + i * RB;
-                if (bb2 < nb && aa < na)
-                    __builtin_nontemporal_store(*reinterpret_cast<const T*>(lds + bb2 * P + aa * W),
-                                                reinterpret_cast<T*>(at<SWZ>(a.dst, off, a.zd)));
+#pragma unroll
+            for (int i0 = 0; i0 < TA / RB; i0 += U2) {
+                T v[U2];
+#pragma unroll
+                for (int u = 0; u < U2; ++u)
+                    v[u] = *reinterpret_cast<const T*>(lds + bb2 * P + (aa2 + (i0 + u) * RB) * W);
+#pragma unroll
+                for (int u = 0; u < U2; ++u) {
+                    if (bb2 < nb && aa2 + (i0 + u) * RB < na)
+                        __builtin_nontemporal_store(v[u], reinterpret_cast<T*>(at<SWZ>(a.dst, off + u * step, a.zd)));
+                }
+                off += U2 * step;
             }
         }
         __syncthreads();   // LDS is reused by the next tile of this workgroup

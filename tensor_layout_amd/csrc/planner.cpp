@@ -392,7 +392,6 @@ static const LdsShape kLdsStrided[] = {
 };
 static constexpr int kTwoPerCuLds = 55 * 1024;
 static constexpr int kThreePerCuLds = 41 * 1024;
-static constexpr int kFourPerCuLds = 33 * 1024;
 
 static std::mutex g_choice_mu;
 
@@ -847,15 +846,16 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             p.block = 256;
             p.grid = l.ntiles;
             p.lds_bytes = !vform ? es->tb * es->pitch() : dst_ok ? es->vrow(es->tb) : es->vbytes();
-            // Launches of 8192 tiles or more in the vector form run at most
-            // four workgroups per CU (reserved LDS): 16384^2 bf16 with source
-            // pitch 16385 (32768 tiles) 206 -> 198 us, u8 16384^2 with pitch
-            // 16387 116 -> 115, fp32 8192^2 with pitch 8193 99.5 -> 96.5,
-            // bf16 16384^2 with destination pitch 16385 346 -> 335; at
-            // 2048-4096 tiles the cap cost up to 27 %, and 1-byte elements in
-            // the shifted form lose 3-5 % with it at any size.
-            if (vform && p.grid >= 8192 && !(w == 1 && !dst_ok) && p.lds_bytes < kFourPerCuLds)
-                p.lds_bytes = kFourPerCuLds;
+            // Launches of 8192 tiles or more in the vector form with aligned
+            // destination rows run at most three workgroups per CU (reserved
+            // LDS): 16384^2 bf16 with source pitch 16385 (32768 tiles) 206 ->
+            // 198 us, u8 16384^2 with pitch 16387 116 -> 114, fp32 8192^2
+            // with pitch 8193 99.4 -> 96.3, bf16 8192^2 with pitch 8196
+            // 52.9 -> 51.6.  At 2048-4096 tiles it cost up to 27 %; the
+            // shifted form gained nothing at three (bf16 16384^2 with
+            // destination pitch 16385) and u8 lost 4 %.
+            if (dst_ok && vform && p.grid >= 8192 && p.lds_bytes < kThreePerCuLds)
+                p.lds_bytes = kThreePerCuLds;
             // a whole item in one tile is read into LDS before any of it is written
             p.unit_is_item = l.ntb == 1 && l.nta == 1;
             return p;

@@ -8,7 +8,9 @@ result with the oracle's.  Written from the kernel's description (tiles of
 TB x TA elements in the tile kernel's order, LDS rows of TA elements plus
 one unit of max(w, 4) bytes, thread t on column t % TA stepping 256 / TA
 rows while loading, on column t % TB stepping 256 / TB rows while
-storing), not shared with it."""
+storing; a lane outside the item loads the tile's first element and
+writes it to its own LDS slot, so that every lane writes in every step),
+not shared with it."""
 
 from __future__ import annotations
 
@@ -44,21 +46,34 @@ def model(x, w, ext, ss, ds, offs, batch, plan_tile, pitch):
             b0, a0 = tbi * TB, tai * TA
             nb, na = min(TB, e_b - b0), min(TA, e_a - a0)
             lds = np.full(TB * pitch, 0xEE, dtype=np.uint8)
+            real = np.zeros(TB * pitch, dtype=bool)
+            junk = np.zeros(TB * pitch, dtype=bool)
+            first = so + b0 * s_b + a0                    # the tile's first element
             for t in range(NT):
                 aa, bb1 = t % TA, t // TA
                 for i in range(TB // RA):
                     bb = bb1 + i * RA
+                    l = bb * pitch + aa * w
+                    assert 0 <= l and l + w <= TB * pitch
+                    assert not real[l:l + w].any() and not junk[l:l + w].any()   # one writer per slot
                     if aa < na and bb < nb:
                         e = so + (b0 + bb) * s_b + a0 + aa
-                        touched_s.add(e)
-                        l = bb * pitch + aa * w
-                        assert 0 <= l and l + w <= TB * pitch
-                        lds[l:l + w] = x[e * w:(e + 1) * w]
+                        real[l:l + w] = True
+                    else:
+                        # every lane writes in every step: one outside the item
+                        # loads the tile's first element into its own slot
+                        e = first
+                        junk[l:l + w] = True
+                    touched_s.add(e)
+                    lds[l:l + w] = x[e * w:(e + 1) * w]
             for t in range(NT):
                 bb, aa2 = t % TB, t // TB
                 for i in range(TA // RB):
                     aa = aa2 + i * RB
+                    l = bb * pitch + aa * w
+                    assert 0 <= l and l + w <= TB * pitch   # every lane reads, in bounds
                     if bb < nb and aa < na:
+                        assert real[l:l + w].all()
                         e = d_o + (a0 + aa) * d_a + b0 + bb
                         touched_d.add(e)
                         l = bb * pitch + aa * w
