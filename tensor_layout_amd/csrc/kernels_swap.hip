@@ -69,8 +69,12 @@ __global__ void __launch_bounds__(T * T * W / (16 * CPT)) k_swap(LdsArgs a) {
         uint8_t* dx = a.dst + qx;
         uint8_t* dy = a.dst + qy;
         if (!a.scalar && hi + T <= a.e_a) {
-            tile_to_lds<W, T, T, CPT, WW>(l0, a.src, px, a.s_b * W, pitch, t, key_w);
-            if (two) tile_to_lds<W, T, T, CPT, WW>(l1, a.src, py, a.s_b * W, pitch, t, key_w);
+            // Both tiles' loads are issued before either is written to LDS.
+            u32x4 vx[CPT], vy[CPT];
+            tile_load<W, T, T, CPT>(vx, a.src, px, a.s_b * W, t);
+            if (two) tile_load<W, T, T, CPT>(vy, a.src, py, a.s_b * W, t);
+            tile_put<W, T, T, CPT, WW>(l0, vx, pitch, t, key_w);
+            if (two) tile_put<W, T, T, CPT, WW>(l1, vy, pitch, t, key_w);
             __syncthreads();
             tile_from_lds<W, T, T, CPT>(l0, a.dst, qx, a.d_a, pitch, t, key_r);
             if (two) tile_from_lds<W, T, T, CPT>(l1, a.dst, qy, a.d_a, pitch, t, key_r);

@@ -23,23 +23,29 @@ __device__ __forceinline__ void unrotate(uint32_t (&d)[N], int key) {
     }
 }
 
-// Phase 1 of an LDS tile: the TB x TA source tile at st (rows srow bytes
+// Phase 1 of an LDS tile: the TB x TA source tile at pt (rows srow bytes
 // apart) through registers into LDS, element (b, a) at b * pitch + a * W.
-// Each thread loads CPT 16-byte chunks, then writes them in 16 / WW pieces
-// whose order is rotated by key_w.
-template <int W, int TB, int TA, int CPT, int WW, bool SWZ = false>
-__device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* gsrc, int64_t pt, int64_t srow, int pitch,
-                                            int t, int key_w, const Swz& z = Swz{}) {
+// Each thread loads CPT 16-byte chunks (tile_load), then writes them in
+// 16 / WW pieces whose order is rotated by key_w (tile_put).
+template <int W, int TB, int TA, int CPT, bool SWZ = false>
+__device__ __forceinline__ void tile_load(u32x4 (&v)[CPT], const uint8_t* gsrc, int64_t pt, int64_t srow, int t,
+                                          const Swz& z = Swz{}) {
     constexpr LdsShape SH{W, TB, TA, CPT};
     constexpr int NT = SH.threads();
     constexpr int CPR = TA * W / 16;
-    constexpr int NP = 16 / WW;   // pieces per chunk
-    u32x4 v[CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const int cid = t + k * NT;
         v[k] = ld16(at<SWZ>(gsrc, pt + (cid / CPR) * srow + (cid % CPR) * 16, z));
     }
+}
+
+template <int W, int TB, int TA, int CPT, int WW>
+__device__ __forceinline__ void tile_put(uint8_t* lds, const u32x4 (&v)[CPT], int pitch, int t, int key_w) {
+    constexpr LdsShape SH{W, TB, TA, CPT};
+    constexpr int NT = SH.threads();
+    constexpr int CPR = TA * W / 16;
+    constexpr int NP = 16 / WW;   // pieces per chunk
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const int cid = t + k * NT;
@@ -62,6 +68,14 @@ __device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* gsrc, i
             }
         }
     }
+}
+
+template <int W, int TB, int TA, int CPT, int WW, bool SWZ = false>
+__device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* gsrc, int64_t pt, int64_t srow, int pitch,
+                                            int t, int key_w, const Swz& z = Swz{}) {
+    u32x4 v[CPT];
+    tile_load<W, TB, TA, CPT, SWZ>(v, gsrc, pt, srow, t, z);
+    tile_put<W, TB, TA, CPT, WW>(lds, v, pitch, t, key_w);
 }
 
 // Phase 2 of an LDS tile: LDS through registers to the destination tile at
