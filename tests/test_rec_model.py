@@ -185,3 +185,22 @@ def test_turn_spreads_piece_lanes_over_all_banks(w, F):
                     assert len(set(banks)) == 32
                 plain = [((q * ce + k) * F + f) * w // 4 % nbanks for q in range(q0, q0 + 32)]
                 assert len(set(plain)) <= 16
+
+
+@pytest.mark.parametrize("F", [1, 3, 5, 7, 9, 17])
+def test_fp32_field_reads_in_lane_order_hit_distinct_banks(F):
+    """Records to fields with 4-byte fields and odd F: lane t of the piece
+    phase reads its piece's records q*4 + (k ^ x) at step k, x = (t >> 3) & 3.
+    The 32 lanes of one read pass (consecutive q, same f and k) touch 32
+    distinct banks (4-byte banks, 32 per pass); in plain record order
+    (x = 0) only 8.  The order is a permutation of each piece's records."""
+    for f in range(F):
+        for k in range(4):
+            for q0 in (0, 32, 96):
+                lanes = range(q0, q0 + 32)
+                banks = [((q * 4 + (k ^ ((q >> 3) & 3))) * F + f) % 32 for q in lanes]
+                assert len(set(banks)) == 32, (F, f, k, q0)
+                plain = [((q * 4 + k) * F + f) % 32 for q in lanes]
+                assert len(set(plain)) == 8
+    for x in range(4):
+        assert sorted(k ^ x for k in range(4)) == [0, 1, 2, 3]
