@@ -523,6 +523,43 @@ def test_element_tiles_full_size():
     check_full("element tiles 16384^2", d.cpu().numpy(), ref)
 
 
+ETILE_LARGE = [
+    # (name, w, extents, src strides, dst strides, src swizzle): launches of
+    # 8192 tiles or more (the three-per-CU reserve of the vector form with
+    # aligned destination rows), the shifted form at that size, and the
+    # element form with its batched loads
+    ("u8_16384sq_src_pitch_16387", 1, (16384, 16384), (16387, 1), (1, 16384), None),
+    ("f32_8192sq_src_pitch_8193", 4, (8192, 8192), (8193, 1), (1, 8192), None),
+    ("bf16_16384sq_dst_pitch_16385", 2, (16384, 16384), (16384, 1), (1, 16385), None),
+    ("u8_8192sq_dst_pitch_8195", 1, (8192, 8192), (8192, 1), (1, 8195), None),
+    ("f64_4096sq_src_pitch_4097", 8, (4096, 4096), (4097, 1), (1, 4096), None),
+    ("bf16_4096sq_src_swizzle_323", 2, (4096, 4096), (4096, 1), (1, 4096), (3, 2, 3)),
+]
+
+
+@pytest.mark.parametrize("case", ETILE_LARGE, ids=lambda c: c[0])
+def test_element_tiles_large(case):
+    """Element tiles at sizes that take the launch-size dependent choices:
+    the whole result against the oracle's."""
+    torch = _torch()
+    name, w, ext, ss, ds, zs = case
+    plan = tpl.tpl_plan(w, ext, ss, ds, src_swizzle=zs)
+    assert plan.kernel == "etile", plan
+    print(f"\n[case] element tiles {name}", flush=True)
+    nbs, nbd = cosize(ext, ss) * w, cosize(ext, ds) * w
+    gen = torch.Generator("cuda").manual_seed(11)
+    x = torch.randint(0, 256, (nbs,), dtype=torch.uint8, device="cuda", generator=gen)
+    d = torch.full((nbd,), SENTINEL, dtype=torch.uint8, device="cuda")
+    tpl.permute(d, x, ext, ss, ds, dtype_bytes=w, src_swizzle=zs)
+    torch.cuda.synchronize()
+    ref = np.full(nbd, SENTINEL, dtype=np.uint8)
+    if zs is None:
+        ref = oracle_threads(x.cpu().numpy(), ref, w, ext, ss, ds, 1)
+    else:
+        oracle.permute(x.cpu().numpy(), ref, w, ext, ss, ds, (0, 0), 1, zs, None)
+    check_full(name, d.cpu().numpy(), ref)
+
+
 # ---------------------------------------------------------------------------
 # The largest rank the ABI takes: 8 modes, permuted axis orders.
 
