@@ -18,10 +18,14 @@ int fail_status(int status, const std::string& why);   // kernels.hip
 typedef uint32_t sx4 __attribute__((ext_vector_type(4)));
 
 // Workgroups (two half-waves each) of the staged kernel; each loops over
-// its share of the items.  On the 2^20-tile SF workload: 4096 (16 per CU)
-// 5.58 TB/s; 2048 3.70, 3072 5.27, 5120 5.44, 8192 5.27, 65536 5.24, one
-// workgroup per two items 3.73.
-constexpr int64_t kStagedGrid = 4096;
+// its share of the items.  On the 2^20-tile SF workload, with the pipelined
+// loop: 3072 (12 per CU) 180.3 us; 2304 193.4, 2560 187.5, 2816 183.2,
+// 3328 179.8, 3584 180.9, 4096 185.1, 8192 211, 16384 229.  The items in
+// flight span a few MiB of each buffer, so the rate also depends on where
+// the buffers lie: with source and destination allocated in another order
+// 3072 took 186.5 us, 3328 184.1, 4096 186.3.  (Before the loop was
+// pipelined 4096 was best, 5.58 TB/s.)
+constexpr int64_t kStagedGrid = 3072;
 
 struct StagedArgs {
     const uint8_t* src;
@@ -69,7 +73,42 @@ __global__ void __launch_bounds__(64) k_staged(StagedArgs a) {
     uint8_t* ls = lds + grp * a.group_bytes;
     uint8_t* ld = ls + a.src_region;
     const tpl_wave::Offsets<P> o = tpl_wave::group_offsets<P>(a.sh, lane, a.shift, a.mask, a.zs, a.zd);
-    for (int64_t first = (int64_t)blockIdx.x * 2; first < a.batch; first += (int64_t)gridDim.x * 2) {
+    const int64_t step = (int64_t)gridDim.x * 2;
+    int64_t first = (int64_t)blockIdx.x * 2;
+    if (a.vec == 16 && a.src_bytes == 32 * 16 && a.dst_bytes == 32 * 16 && first + 1 < a.batch) {
+        // Items of one 16-byte chunk per lane each way, software pipelined
+        // over the iterations in which both half-waves have an item: the
+        // next item's chunk is loaded while this one is permuted and stored.
+        // Every load and store of the loop is unconditional (a load past
+        // the last item reads the last item again), so the wait for the
+        // next chunk before it enters LDS does not also wait for the store
+        // issued after that load.
+        const uint8_t* sp = a.src + lane * 16;
+        const int64_t last = a.batch - 1;
+        *reinterpret_cast<sx4*>(ls + lane * 16) =
+            *reinterpret_cast<const sx4*>(sp + (first + grp) * a.span_s);
+        sx4 v = *reinterpret_cast<const sx4*>(sp + min(first + step + grp, last) * a.span_s);
+        auto iteration = [&]() {
+            __syncthreads();
+            tpl_wave::group_permute<T, P>(reinterpret_cast<T*>(ld), reinterpret_cast<const T*>(ls), o);
+            __syncthreads();
+            const sx4 r = *reinterpret_cast<const sx4*>(ld + lane * 16);
+            const bool more = first + step + 1 < a.batch;   // the next iteration is full too
+            if (more) {
+                *reinterpret_cast<sx4*>(ls + lane * 16) = v;
+                v = *reinterpret_cast<const sx4*>(sp + min(first + 2 * step + grp, last) * a.span_s);
+            }
+            *reinterpret_cast<sx4*>(a.dst + (first + grp) * a.span_d + lane * 16) = r;
+            first += step;
+            return more;
+        };
+        // The first iteration runs on its own, so that the loop is entered,
+        // as it is re-entered, with a load and then a store outstanding.
+        if (iteration())
+            while (iteration()) {
+            }
+    }
+    for (; first < a.batch; first += step) {
         const int64_t item = first + grp;
         const bool act = item < a.batch;   // uniform across the half-wave
         if (act) group_copy_v(ls, a.src + item * a.span_s, a.src_bytes, lane, a.vec);
