@@ -55,6 +55,13 @@ CASES = [
     ("32x32_fp32", 4, (32, 32), (32, 1), (1, 32), 65),
     ("16x64_fp16", 2, (16, 64), (64, 1), (1, 16), 77),
     ("4d_axes0231_u16", 2, (2, 4, 4, 8), (128, 32, 8, 1), (128, 1, 32, 4), 33),
+    # items of one 16-byte chunk per lane take the pipelined loop: several
+    # full iterations per workgroup (3072 workgroups move 6144 items per
+    # iteration), then a partial one with an odd item count, or none
+    ("sf_fp32_pipelined_odd_tail", 4, (4, 32), (32, 1), (1, 4), 3 * 6144 + 1001),
+    ("sf_fp32_pipelined_whole", 4, (4, 32), (32, 1), (1, 4), 2 * 6144),
+    ("8x32_fp16_pipelined", 2, (8, 32), (32, 1), (1, 8), 6144 + 1),
+    ("16x32_u8_pipelined", 1, (16, 32), (32, 1), (1, 16), 5 * 6144 - 3),
 ]
 
 
