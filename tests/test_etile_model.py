@@ -98,7 +98,29 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"w{c[0]}_{c[1]}")
+def _random_cases(n, seed):
+    """Seeded small 2-D transposes that plan as element tiles: 8-byte
+    elements with unaligned pitches (the element form runs them), and 1- to
+    4-byte ones (the element form runs those when an operand is swizzled;
+    the model here replays the same tiles without the swizzle map)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        w = int(rng.choice([1, 2, 4, 8, 8]))
+        eb, ea = int(rng.integers(8, 200)), int(rng.integers(8, 200))
+        ps = ea + int(rng.integers(0, 5))
+        pd = eb + int(rng.integers(0, 5))
+        offs = (int(rng.integers(0, 4)), int(rng.integers(0, 4)))
+        batch = int(rng.integers(1, 3))
+        case = (w, (eb, ea), (ps, 1), (1, pd), offs, batch)
+        p = tpl.tpl_plan(w, case[1], case[2], case[3], offs, batch)
+        if p.ok and p.kernel == "etile":
+            out.append(case)
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(16, 77),
+                         ids=lambda c: f"w{c[0]}_{c[1]}_{c[2][0]}_{c[3][1]}_{c[4]}_{c[5]}")
 def test_etile_model(case):
     w, ext, ss, ds, offs, batch = case
     p = tpl.tpl_plan(w, ext, ss, ds, offs, batch)

@@ -196,7 +196,27 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: f"w{c[0]}_{c[1]}_{c[4]}")
+def _random_cases(n, seed):
+    """Seeded small 2-D transposes with unaligned pitches or offsets on
+    either side (the plan must take the vector form of the element tiles)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        w = int(rng.choice([1, 2, 4]))
+        eb, ea = int(rng.integers(8, 300)), int(rng.integers(8, 300))
+        ps = ea + int(rng.integers(0, 9))       # source row pitch (elements)
+        pd = eb + int(rng.integers(0, 9))       # destination row pitch
+        offs = (int(rng.integers(0, 8)), int(rng.integers(0, 8)))
+        batch = int(rng.integers(1, 3))
+        case = (w, (eb, ea), (ps, 1), (1, pd), offs, batch)
+        p = tpl.tpl_plan(w, case[1], case[2], case[3], offs, batch)
+        if p.ok and p.kernel == "etile":
+            out.append(case)
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(24, 2024),
+                         ids=lambda c: f"w{c[0]}_{c[1]}_{c[2][0]}_{c[3][1]}_{c[4]}_{c[5]}")
 def test_etile_vector_model(case):
     w, ext, ss, ds, offs, batch = case
     p = tpl.tpl_plan(w, ext, ss, ds, offs, batch)
