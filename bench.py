@@ -330,10 +330,10 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
 
     # Reference first: a plain copy of the same bytes (the library's
     # identity-layout copy, 16-byte vectors) over the same buffer rotation,
-    # 200 launches between two events.  Run before the warm-up, it also
-    # brings the GPU out of idle clocks, so that a short timed run (a few
-    # launches) sees the same clocks as a long one; the outputs it writes
-    # are cleared before the permute's launches.
+    # 200 launches between two events after at least 30 ms of untimed ones.
+    # Run before the warm-up, it also brings the GPU out of idle clocks, so
+    # that a short timed run (a few launches) sees the same clocks as a long
+    # one; the outputs it writes are cleared before the permute's launches.
     ceiling = None
     if do_ceiling and nbytes % 16 == 0 and nbytes <= min(ns, nd) and entry == "permute":
         ident = tpl.PreparedPermute(16, (nbytes // 16,), (1,), (1,))
@@ -341,9 +341,15 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
         cptrs = [(srcs[i].data_ptr(), (srcs[(i + 1) % pairs] if wl.inplace else dsts[i]).data_ptr())
                  for i in range(pairs)]
         csteps = 200
-        for i in range(10):
-            ident(*cptrs[i % pairs], sp)
-        torch.cuda.synchronize()
+        # untimed copies for at least 30 ms of GPU time, so that small
+        # workloads are timed at load clocks too
+        t_warm = time.perf_counter() + 0.03
+        i = 0
+        while i < 10 or time.perf_counter() < t_warm:
+            for _ in range(10):
+                ident(*cptrs[i % pairs], sp)
+                i += 1
+            torch.cuda.synchronize()
         c0 = torch.cuda.Event(enable_timing=True)
         c1 = torch.cuda.Event(enable_timing=True)
         c0.record(stream)
