@@ -189,6 +189,33 @@ def device_memory_props():
             "clock_x_bus_x2_over_8_gbps": round(clk.value * 1e3 * bus.value * 2 / 8 / 1e9, 1)}
 
 
+def device_info():
+    """The device and software the line was measured on: the device name,
+    its gfx target and CU count as torch reports them, the HIP runtime and
+    driver versions (hipRuntimeGetVersion, hipDriverGetVersion) and torch's
+    HIP build."""
+    import ctypes
+    import torch
+    info = {}
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        info.update(name=pr.name, gcn_arch=getattr(pr, "gcnArchName", None),
+                    compute_units=pr.multi_processor_count, total_memory_bytes=pr.total_memory)
+    except Exception:   # noqa: BLE001 -- reported as absent
+        pass
+    try:
+        lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+        rt, drv = ctypes.c_int(), ctypes.c_int()
+        if lib.hipRuntimeGetVersion(ctypes.byref(rt)) == 0:
+            info["hip_runtime_version"] = rt.value
+        if lib.hipDriverGetVersion(ctypes.byref(drv)) == 0:
+            info["hip_driver_version"] = drv.value
+    except OSError:
+        pass
+    info["torch_hip"] = getattr(torch.version, "hip", None)
+    return info
+
+
 def cpu_baseline(wl, x, min_seconds=10.0, max_runs=100):
     """The oracle as it stands, single-threaded, on the full workload."""
     import numpy as np
@@ -441,6 +468,7 @@ def bench_one(wl, steps, warmup, do_cpu, do_verify, entry="permute", xor_k=-1, d
             "per_launch": per_launch,
             "device_memory": device_memory_props(),
         },
+        "device": device_info(),
     }
     ref = None
     if do_cpu:
