@@ -20,7 +20,10 @@ namespace tpl {
 // order j = r ^ ((lane >> shift_r) & mask_r), restores row order in
 // registers, packs sub-dword elements into destination-order dwords and
 // stores 16 bytes.  Both XORs are the planner's smallest conflict-free k for
-// the measured gfx950 LDS banks.
+// the measured gfx950 LDS banks.  Tiles of 4- to 16-byte elements store with
+// device scope (st16_dev): 4096^2 x 16 B 90.3 -> 88.0 us, the 16 MiB and
+// 32 MiB 4-D permutes 1.2 % faster; 1- and 2-byte tiles measured the same or
+// up to 2 % slower that way and keep st16.
 
 template <int W, int TB, int TA, int CPT, int WW, int NB, bool BIG, bool SWZ>
 __device__ __forceinline__ void lds_loop(const LdsArgs& a, uint8_t* lds) {
@@ -65,17 +68,19 @@ __device__ __forceinline__ void lds_loop(const LdsArgs& a, uint8_t* lds) {
         tile_to_lds<W, TB, TA, CPT, WW, SWZ>(lds, a.src, (so + b0 * a.s_b + a0) * W, a.s_b * W, pitch, t, key_w,
                                              a.zs);
         __syncthreads();
-        tile_from_lds<W, TB, TA, CPT, SWZ>(lds, a.dst, (d_o + a0 * a.d_a + b0) * W, a.d_a, pitch, t, key_r, a.zd);
+        tile_from_lds<W, TB, TA, CPT, SWZ, (W >= 4)>(lds, a.dst, (d_o + a0 * a.d_a + b0) * W, a.d_a, pitch, t, key_r,
+                                                    a.zd);
         __syncthreads();   // LDS is reused by the next tile of this workgroup
     }
 }
 
-template <int W, int TB, int TA, int CPT, int WW, int NB, bool BIG>
+// Plain and swizzled operands are separate kernels: with both loops in one
+// kernel behind a uniform branch, the plain fp16 tile workload (65536 tiles
+// of 128 x 64) ran 342.3 us against 337.7 for the plain loop alone.
+template <int W, int TB, int TA, int CPT, int WW, int NB, bool BIG, bool SWZ>
 __global__ void __launch_bounds__(TB * TA * W / (16 * CPT)) k_lds(LdsArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    // Plain operands take the code without swizzle arithmetic (a uniform branch).
-    if ((a.zs.ymask | a.zd.ymask) == 0) lds_loop<W, TB, TA, CPT, WW, NB, BIG, false>(a, lds);
-    else lds_loop<W, TB, TA, CPT, WW, NB, BIG, true>(a, lds);
+    lds_loop<W, TB, TA, CPT, WW, NB, BIG, SWZ>(a, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -85,10 +90,12 @@ template <int W, int NB, bool BIG>
 hipError_t launch_lds_width(const Plan& p, const LdsArgs& a, hipStream_t st) {
     dim3 grid((unsigned)cap_grid(p.grid, p.block)), block((unsigned)p.block);
     const int tb = p.tile_b, ta = p.tile_a, cpt = p.cpt, ww = p.ww;
-#define TPL_LDS_CASE(W_, TB_, TA_, CPT_, WW_)                                                          \
-    if (tb == TB_ && ta == TA_ && cpt == CPT_ && ww == WW_) {                                 \
-        hipLaunchKernelGGL((k_lds<W_, TB_, TA_, CPT_, WW_, NB, BIG>), grid, block, p.lds_bytes, st, a); \
-        return hipGetLastError();                                                                        \
+    const bool swz = (a.zs.ymask | a.zd.ymask) != 0;
+#define TPL_LDS_CASE(W_, TB_, TA_, CPT_, WW_)                                                                \
+    if (tb == TB_ && ta == TA_ && cpt == CPT_ && ww == WW_) {                                                \
+        if (swz) hipLaunchKernelGGL((k_lds<W_, TB_, TA_, CPT_, WW_, NB, BIG, true>), grid, block, p.lds_bytes, st, a); \
+        else hipLaunchKernelGGL((k_lds<W_, TB_, TA_, CPT_, WW_, NB, BIG, false>), grid, block, p.lds_bytes, st, a);   \
+        return hipGetLastError();                                                                              \
     }
 #define TPL_LDS_SHAPE(W_, TB_, TA_, CPT_) \
     TPL_LDS_CASE(W_, TB_, TA_, CPT_, 16) TPL_LDS_CASE(W_, TB_, TA_, CPT_, 8) TPL_LDS_CASE(W_, TB_, TA_, CPT_, 4)

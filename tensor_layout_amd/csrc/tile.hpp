@@ -89,7 +89,8 @@ __device__ __forceinline__ void tile_to_lds(uint8_t* lds, const uint8_t* gsrc, i
 // arithmetic and stores, which measured 2-4 % slower on the 16384^2 bf16
 // transpose at two workgroups per CU (183.6 us interleaved group by group,
 // 181.2 us with address arithmetic between the stores, 176.7 us unbroken).
-template <int W, int TB, int TA, int CPT, bool SWZ = false>
+// DEV selects the device-scope non-temporal store (st16_dev) over st16.
+template <int W, int TB, int TA, int CPT, bool SWZ = false, bool DEV = false>
 __device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* gdst, int64_t pt, int64_t d_a, int pitch,
                                               int t, int key_r, const Swz& z = Swz{}) {
     constexpr LdsShape SH{W, TB, TA, CPT};
@@ -182,7 +183,10 @@ __device__ __forceinline__ void tile_from_lds(const uint8_t* lds, uint8_t* gdst,
     for (int k2 = 0; k2 < GPT; ++k2)
         if (live[k2])
 #pragma unroll
-            for (int s2 = 0; s2 < NS; ++s2) st16(dst[k2][s2], o[k2][s2]);
+            for (int s2 = 0; s2 < NS; ++s2) {
+                if constexpr (DEV) st16_dev(dst[k2][s2], o[k2][s2]);
+                else st16(dst[k2][s2], o[k2][s2]);
+            }
 }
 
 // One element of W bytes, moved in pieces of min(W, 4) bytes (the LDS pitch

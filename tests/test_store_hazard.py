@@ -24,7 +24,7 @@ import pytest
 
 from tensor_layout_amd import build
 
-SOURCES = ["kernels_quad.hip", "kernels_stream.hip"]
+SOURCES = ["kernels_quad.hip", "kernels_stream.hip", "kernels_lds_w48.hip", "kernels_lds_w16.hip"]
 WAIT_STATES = 2
 
 _REG_RANGE = re.compile(r"^v\[(\d+):(\d+)\]$")
