@@ -185,6 +185,22 @@ constexpr EtileShape kEtileShapes[5] = {
 };
 constexpr TPL_HD int etile_index(int w) { return w == 1 ? 0 : w == 2 ? 1 : w == 4 ? 2 : w == 8 ? 3 : 4; }
 
+// Tall vector-form tiles: twice the rows, so destination row pieces of 256
+// bytes (u8) and 512 bytes (bf16), and half the extra rows per tile that
+// unaligned destination rows need.  The placement constants were searched
+// on the same CPU model of the gfx950 passes.  bf16 writes LDS in 4-byte
+// pieces: with 8- or 16-byte pieces the row pitch and skew are multiples of
+// 8 bytes, and the 32 rows one column's half-wave reads then fall on 16
+// banks.  The search found no conflict-free tall placement for 4-byte
+// elements (256 x 32).
+constexpr EtileShape kEtileTall[2] = {
+    {1, 256, 128, 152, 8, 4, 8},
+    {2, 256, 64, 148, 4, 3, 4},
+};
+constexpr TPL_HD EtileShape etile_vshape(int w, bool tall) {
+    return tall && w <= 2 ? kEtileTall[w - 1] : kEtileShapes[etile_index(w)];
+}
+
 // In-place pair swaps walk tile pairs in blocks of kSwapG x kSwapG tiles.
 constexpr int kSwapLogG = 3;
 constexpr int kSwapG = 1 << kSwapLogG;

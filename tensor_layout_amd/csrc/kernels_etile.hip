@@ -115,11 +115,12 @@ __device__ __forceinline__ void etile_loop(const LdsArgs& a, uint8_t* lds) {
 // step.  Partial chunks, stored element by element, are left only at an
 // item's first and last rows.  SHIFT = false compiles the case where every
 // destination row is on 16 bytes (delta = 0, TB rows) without the shift
-// arithmetic.
-template <int W, int NB, bool BIG, bool SHIFT, int G>
+// arithmetic.  TALL takes the tall tile of the width (kEtileTall).
+template <int W, int NB, bool BIG, bool SHIFT, bool TALL, int G>
 __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
     typedef typename Elem<W>::type T;
-    constexpr EtileShape ES = kEtileShapes[etile_index(W)];
+    static_assert(!TALL || W <= 2, "tall tiles exist for 1- and 2-byte elements");
+    constexpr EtileShape ES = etile_vshape(W, TALL);
     constexpr int TB = ES.tb, TA = ES.ta, NT = 256, E = 16 / W;
     constexpr int QS = TA * W / 16, QD = TB * W / 16;   // chunks of a whole source / destination row piece
     constexpr int RS = NT / QS, CS = NT / QD;           // rows / columns per step
@@ -311,20 +312,20 @@ __device__ __forceinline__ void etile_vec_loop(const LdsArgs& a, uint8_t* lds) {
 // the shifted form, where each element holds a register until packed (all
 // four steps took 178 VGPRs and ran 6 % slower than the one-step form on
 // u8 16384^2 with destination pitch 16387; two steps 1 % slower).
-template <int W, bool SHIFT>
+template <int W, bool SHIFT, bool TALL>
 constexpr int etile_read_group() {
-    constexpr EtileShape ES = kEtileShapes[etile_index(W)];
+    constexpr EtileShape ES = etile_vshape(W, TALL);
     constexpr int ND = ES.ta / (256 / (ES.tb * W / 16));
     return W == 1 && SHIFT ? 1 : ND;
 }
 
 // The two forms are separate kernels: the element form's swizzle branch
 // would otherwise set the vector form's register count.
-template <int W, int NB, bool BIG, bool SHIFT, int G_ = etile_read_group<W, SHIFT>()>
+template <int W, int NB, bool BIG, bool SHIFT, bool TALL, int G_ = etile_read_group<W, SHIFT, TALL>()>
 __global__ void __launch_bounds__(256) k_etile_vec(LdsArgs a) {
     // the plan's LDS bytes: vrow(TB) (vrow(TB + 16 / W - 1) shifted) or more
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    etile_vec_loop<W, NB, BIG, SHIFT, G_>(a, lds);
+    etile_vec_loop<W, NB, BIG, SHIFT, TALL, G_>(a, lds);
 }
 
 template <int W, int NB, bool BIG>
@@ -339,6 +340,21 @@ __global__ void __launch_bounds__(256) k_etile(LdsArgs a) {
 // Launcher: the plan picks the form (plain operands of up to 4 bytes take
 // the vector form).
 
+// The vector form of width W: aligned (vform 1) or shifted (2) destination
+// rows, the width's tile or its tall tile (the plan's TB says which).
+template <int W, int NB, bool BIG>
+static void launch_etile_vec(const Plan& p, const LdsArgs& a, dim3 grid, dim3 block, hipStream_t st) {
+    constexpr bool CT = W <= 2;   // a tall tile exists
+    const bool tall = CT && p.tile_b == etile_vshape(W, true).tb;
+    if (a.vform == 1) {
+        if (tall) hipLaunchKernelGGL((k_etile_vec<W, NB, BIG, false, CT>), grid, block, p.lds_bytes, st, a);
+        else hipLaunchKernelGGL((k_etile_vec<W, NB, BIG, false, false>), grid, block, p.lds_bytes, st, a);
+    } else {
+        if (tall) hipLaunchKernelGGL((k_etile_vec<W, NB, BIG, true, CT>), grid, block, p.lds_bytes, st, a);
+        else hipLaunchKernelGGL((k_etile_vec<W, NB, BIG, true, false>), grid, block, p.lds_bytes, st, a);
+    }
+}
+
 template <int NB, bool BIG>
 hipError_t launch_etile(const Plan& p, const uint8_t* src, uint8_t* dst, hipStream_t st) {
     LdsArgs a = p.lds;
@@ -347,9 +363,8 @@ hipError_t launch_etile(const Plan& p, const uint8_t* src, uint8_t* dst, hipStre
     dim3 grid((unsigned)cap_grid(p.grid, 256)), block(256);
 #define TPL_ETILE_CASE(W_)                                                                   \
     case W_:                                                                                 \
-        if (a.vform == 1) hipLaunchKernelGGL((k_etile_vec<W_, NB, BIG, false>), grid, block, p.lds_bytes, st, a); \
-        else if (a.vform == 2) hipLaunchKernelGGL((k_etile_vec<W_, NB, BIG, true>), grid, block, p.lds_bytes, st, a); \
-        else hipLaunchKernelGGL((k_etile<W_, NB, BIG>), grid, block, p.lds_bytes, st, a);              \
+        if (a.vform != 0) launch_etile_vec<W_, NB, BIG>(p, a, grid, block, st);             \
+        else hipLaunchKernelGGL((k_etile<W_, NB, BIG>), grid, block, p.lds_bytes, st, a);   \
         break;
     switch (p.w) {
         TPL_ETILE_CASE(1)

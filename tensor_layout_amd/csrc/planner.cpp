@@ -350,6 +350,12 @@ const EtileShape* etile_shape(int w) {
     return nullptr;
 }
 
+const EtileShape* etile_tall_shape(int w) {
+    for (const EtileShape& e : kEtileTall)
+        if (e.w == w) return &e;
+    return nullptr;
+}
+
 // Tile shapes the library instantiates: (w, TB, TA, CPT), largest first.
 // Two 16-byte chunks per thread: measured a little faster than four on the
 // large transposes (more waves, each with less data in flight).
@@ -819,6 +825,25 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
         const EtileShape* es = etile_shape(w);
         if (es && sa % w == 0 && da % w == 0 && ma.e >= 8 && mb.e >= 8) {
             p.kernel = TPL_KERNEL_ETILE;
+            // Plain operands take the kernel's vector form (16-byte chunks
+            // kept in LDS as read), swizzled ones its element form.
+            const bool vform = plain && w <= 4;
+            int64_t items = 1;
+            for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
+            // Tall tiles (twice the rows) where they measured faster: the
+            // shifted form at 2048 tall tiles or more (u8 8192^2 with
+            // destination pitch 8195 75 -> 53 us, bf16 8192^2 with pitch 8193
+            // 84 -> 71, u8 and bf16 16384^2 with pitches 16387 and 16385 258 ->
+            // 183 and 352 -> 251; bf16 4096^2 with pitch 4097, 1024 tall
+            // tiles, 21.3 -> 22.0), and bf16 with aligned destination rows at
+            // 16384 or more (16384^2 with source pitch 16385 198.8 -> 195.0;
+            // 8192^2 with pitch 8196, 4096 tall tiles, 51.3 -> 56.1; u8
+            // 16384^2 with pitch 16387 113 -> 116).
+            if (vform && w <= 2) {
+                const EtileShape* tall = etile_tall_shape(w);
+                const int64_t nt = items * ((mb.e + tall->tb - 1) / tall->tb) * ((ma.e + tall->ta - 1) / tall->ta);
+                if ((!dst_ok && nt >= 2048) || (dst_ok && w == 2 && nt >= 16384)) es = tall;
+            }
             LdsArgs& l = p.lds;
             l = LdsArgs{};
             l.e_b = mb.e;
@@ -827,16 +852,11 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
             l.d_a = ma.d;
             l.ntb = (mb.e + es->tb - 1) / es->tb;
             l.nta = (ma.e + es->ta - 1) / es->ta;
-            int64_t items = 1;
-            for (int i = 0; i < no; ++i) items *= sh.m[others[i]].e;
             l.ntiles = items * l.ntb * l.nta;
             if (l.ntiles >= ((int64_t)1 << 31)) p.big = true;
             l.div_nta = make_fastdiv((uint32_t)std::min<int64_t>(l.nta, 0x7fffffff));
             l.div_ntb = make_fastdiv((uint32_t)std::min<int64_t>(l.ntb, 0x7fffffff));
             set_modes(l.batch, sh, others, no);
-            // Plain operands take the kernel's vector form (16-byte chunks
-            // kept in LDS as read), swizzled ones its element form.
-            const bool vform = plain && w <= 4;
             l.pitch = vform ? es->rp : es->pitch();
             l.vform = !vform ? 0 : dst_ok ? 1 : 2;
             p.tile_b = es->tb;

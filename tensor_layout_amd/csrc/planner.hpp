@@ -100,6 +100,7 @@ const LdsShape* swap_shapes(int* n);
 
 // The element-tile shape for width w (nullptr for other widths).
 const EtileShape* etile_shape(int w);
+const EtileShape* etile_tall_shape(int w);   // nullptr for widths without one
 
 // The pages' method on one warp region (32 lanes, 32 banks).
 Plan plan_pages32(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,

@@ -44,18 +44,22 @@ NT = 256
 ALIGN = 256
 # w: (TB, TA, rp, sk, le, g)
 VSHAPES = {1: (128, 128, 144, 16, 4, 16), 2: (128, 64, 152, 8, 3, 8), 4: (128, 32, 148, 4, 2, 4)}
+# The tall tiles of 1- and 2-byte elements (twice the rows), which the
+# planner takes for large launches.
+TALL = {1: (256, 128, 152, 8, 4, 8), 2: (256, 64, 148, 4, 3, 4)}
 
 
 def vrow(bb, rp, sk, le):
     return bb * rp + sk * (bb >> le)
 
 
-def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None):
+def model(x, w, ext, ss, ds, offs, batch, item_strides=None, out=None, shape=None):
     """Replay the vector form on a 2-mode (plus batch) layout; buffers at
     ALIGN-aligned addresses, element offsets in offs.  Batch items lie one
     span apart unless item_strides = (source, destination) says otherwise;
-    `out` (the destination buffer) may be given, else one of 0xCD bytes."""
-    TB, TA, rp, sk, le, g = VSHAPES[w]
+    `out` (the destination buffer) may be given, else one of 0xCD bytes.
+    `shape` (TB, TA, rp, sk, le, g) defaults to the width's tile."""
+    TB, TA, rp, sk, le, g = shape or VSHAPES[w]
     QS, QD = TA * w // 16, TB * w // 16
     RS, CS = NT // QS, NT // QD
     a_mode = [i for i, s in enumerate(ss) if s == 1][0]
@@ -238,6 +242,65 @@ def test_etile_vector_model(case):
     assert np.array_equal(out, ref)
 
 
+def _tall_cases(n, seed):
+    """Seeded small 2-D transposes of 1- and 2-byte elements with unaligned
+    pitches or offsets, replayed with the tall tiles (the planner takes them
+    only for large launches, so the model runs them on small ones)."""
+    rng = np.random.default_rng(seed)
+    out = [(2, (300, 140), (141, 1), (1, 303), (0, 0), 1), (1, (600, 140), (141, 1), (1, 605), (3, 1), 1),
+           (2, (260, 70), (73, 1), (1, 260), (0, 0), 2), (1, (257, 129), (131, 1), (1, 257), (0, 0), 1)]
+    while len(out) < n:
+        w = int(rng.choice([1, 2]))
+        eb, ea = int(rng.integers(8, 700)), int(rng.integers(8, 300))
+        ps = ea + int(rng.integers(0, 9))
+        pd = eb + int(rng.integers(0, 9))
+        offs = (int(rng.integers(0, 8)), int(rng.integers(0, 8)))
+        if (ps * w) % 16 == 0 and (pd * w) % 16 == 0 and (offs[0] * w) % 16 == 0 and (offs[1] * w) % 16 == 0:
+            continue
+        out.append((w, (eb, ea), (ps, 1), (1, pd), offs, int(rng.integers(1, 3))))
+    return out
+
+
+@pytest.mark.parametrize("case", _tall_cases(20, 4096),
+                         ids=lambda c: f"w{c[0]}_{c[1]}_{c[2][0]}_{c[3][1]}_{c[4]}_{c[5]}")
+def test_etile_tall_model(case):
+    w, ext, ss, ds, offs, batch = case
+    span_s = 1 + sum((e - 1) * s for e, s in zip(ext, ss))
+    span_d = 1 + sum((e - 1) * d for e, d in zip(ext, ds))
+    x = synth.random_bytes(12, (offs[0] + batch * span_s) * w).copy()
+    ref = np.full((offs[1] + batch * span_d) * w, 0xCD, dtype=np.uint8)
+    oracle.permute(x, ref, w, ext, ss, ds, offs, batch)
+    out, chunks, stored = model(x, w, ext, ss, ds, offs, batch, shape=TALL[w])
+    fp_s = footprint(ext, ss, batch, span_s, offs[0])
+    for A in set(chunks):
+        assert any((A + k) // w in fp_s for k in range(0, 16, w)), A
+    assert sorted(stored) == sorted(footprint(ext, ds, batch, span_d, offs[1]))
+    assert np.array_equal(out, ref)
+
+
+def test_etile_tall_planner_choice():
+    """The planner's rule: tall tiles for unaligned destination rows from 2048
+    tall tiles, for bf16 with aligned destination rows from 16384; the plan
+    reports the tall tile's placement."""
+    cases = [
+        # w, extents, src strides, dst strides, tall
+        (2, (8192, 8192), (8192, 1), (1, 8193), True),
+        (2, (4096, 4096), (4096, 1), (1, 4097), False),     # 1024 tall tiles
+        (1, (8192, 8192), (8192, 1), (1, 8195), True),      # 2048
+        (1, (4096, 8192), (8192, 1), (1, 4099), False),     # 1024
+        (2, (16384, 16384), (16385, 1), (1, 16384), True),  # aligned destination, 16384
+        (2, (8192, 8192), (8196, 1), (1, 8192), False),     # aligned destination, 4096
+        (1, (16384, 16384), (16387, 1), (1, 16384), False),  # u8 with aligned destination rows
+        (4, (8192, 8192), (8192, 1), (1, 8193), False),     # no tall 4-byte tile
+        (2, (8000, 8100), (8100, 1), (1, 8003), True),      # ragged both ways
+    ]
+    for w, ext, ss, ds, tall in cases:
+        p = tpl.tpl_plan(w, ext, ss, ds)
+        assert p.ok and p.kernel == "etile", (ext, p)
+        TB, TA, rp, sk, le, g = TALL[w] if tall else VSHAPES[w]
+        assert tuple(p.tile) == (TB, TA) and p.lds_pitch == rp, (w, ext, ss, ds, p)
+
+
 def ways(addrs, width, nbanks):
     used = {}
     for a in addrs:
@@ -246,17 +309,25 @@ def ways(addrs, width, nbanks):
     return max(len(s) for s in used.values())
 
 
-@pytest.mark.parametrize("w", [1, 2, 4])
-@pytest.mark.parametrize("pm", [0, 2, 8, 14])
-def test_etile_vector_lds_is_conflict_free(w, pm):
+def ways_aligned(addrs, width, nbanks):
+    """ways() for accesses aligned to their width: an element of 1 or 2
+    bytes then lies in one dword (ways() counts the 4 bytes from its
+    address, which may reach into the next dword)."""
+    used = {}
+    for a in addrs:
+        assert a % width == 0
+        for dw in range(a // 4, (a + width - 1) // 4 + 1):
+            used.setdefault(dw % nbanks, set()).add(dw)
+    return max(len(s) for s in used.values())
+
+
+def check_banks(w, shape, pm, read_ways):
     """Measured gfx950 passes: b128 writes 8 lanes, b64 writes 16 lanes (32
     banks), b32 writes and reads of up to 4 bytes 32 lanes (32 banks); lanes
-    on one dword share it.  pm: the change of
-    a source row's lead per row (the source row pitch in bytes mod 16); the
-    destination is aligned."""
-    if pm % w:
-        pytest.skip("leads are multiples of the element width")
-    TB, TA, rp, sk, le, g = VSHAPES[w]
+    on one dword share it.  pm: the change of a source row's lead per row
+    (the source row pitch in bytes mod 16); the destination is aligned.
+    read_ways counts the element reads of phase 2."""
+    TB, TA, rp, sk, le, g = shape
     QS, QD = TA * w // 16, TB * w // 16
     for L0 in sorted({0, (3 * w) % 16}):
         lead = lambda bb: (L0 + bb * pm) % 16
@@ -293,8 +364,7 @@ def test_etile_vector_lds_is_conflict_free(w, pm):
             for ps in passes:
                 assert ways(ps, g, 32) == 1, (w, "extra", p0)
         # phase 2: element j of one wave's chunks (lane -> chunk lane % QD of column lane // QD)
-        nbanks = 32
-        for c0 in range(0, TA, 64 // QD):
+        for c0 in range(0, TA, max(1, 64 // QD)):
             for j in range(16 // w):
                 for first in (0, 32):
                     addrs = []
@@ -303,7 +373,24 @@ def test_etile_vector_lds_is_conflict_free(w, pm):
                         bb = q * (16 // w) + j
                         if aa < TA and bb < TB:
                             addrs.append(vrow(bb, rp, sk, le) + lead(bb) + aa * w)
-                    assert ways(addrs, w, nbanks) == 1, (w, pm, L0, c0, j, first)
+                    assert read_ways(addrs, w, 32) == 1, (w, pm, L0, c0, j, first)
+
+
+@pytest.mark.parametrize("w", [1, 2, 4])
+@pytest.mark.parametrize("pm", [0, 2, 8, 14])
+def test_etile_vector_lds_is_conflict_free(w, pm):
+    if pm % w:
+        pytest.skip("leads are multiples of the element width")
+    check_banks(w, VSHAPES[w], pm, ways)
+
+
+@pytest.mark.parametrize("w", [1, 2])
+def test_etile_tall_lds_is_conflict_free(w):
+    """The tall tiles over every lead step: phase 1 on the same pass model;
+    phase 2 has 32 rows of one column per half-wave (bf16) or 16 rows of two
+    (bytes), so element reads are counted by the dword that holds them."""
+    for pm in range(0, 16, w):
+        check_banks(w, TALL[w], pm, ways_aligned)
 
 
 def test_etile_vector_shapes_match_the_library():
@@ -318,12 +405,14 @@ def test_etile_vector_shapes_match_the_library():
 
 def test_etile_vector_lead_sweep_is_conflict_free():
     """Phase 2 over every tile lead L0 and every per-row lead step pm (the
-    source pitch in bytes mod 16), aligned destination."""
-    for w, (TB, TA, rp, sk, le, g) in VSHAPES.items():
+    source pitch in bytes mod 16), aligned destination; the tall tiles with
+    element reads counted by the dword that holds them."""
+    shapes = [(w, sh, ways) for w, sh in VSHAPES.items()] + [(w, sh, ways_aligned) for w, sh in TALL.items()]
+    for w, (TB, TA, rp, sk, le, g), count in shapes:
         QD = TB * w // 16
         for pm in range(0, 16, w):
             for L0 in range(0, 16, w):
-                for c0 in range(0, TA, 64 // QD):
+                for c0 in range(0, TA, max(1, 64 // QD)):
                     for j in range(16 // w):
                         for first in (0, 32):
                             addrs = []
@@ -331,7 +420,7 @@ def test_etile_vector_lead_sweep_is_conflict_free():
                                 q, aa = lane % QD, c0 + lane // QD
                                 bb = q * (16 // w) + j
                                 addrs.append(vrow(bb, rp, sk, le) + (L0 + bb * pm) % 16 + aa * w)
-                            assert ways(addrs, w, 32) == 1, (w, pm, L0, c0, j, first)
+                            assert count(addrs, w, 32) == 1, (w, TB, pm, L0, c0, j, first)
 
 
 @pytest.mark.parametrize("w,n,pitch,batch,gap,offset", [(1, 100, 101, 7, 0, 0), (2, 60, 61, 9, 3, 1), (4, 30, 33, 4, 5, 2)])

@@ -532,6 +532,12 @@ ETILE_LARGE = [
     ("f32_8192sq_src_pitch_8193", 4, (8192, 8192), (8193, 1), (1, 8192), None),
     ("bf16_16384sq_dst_pitch_16385", 2, (16384, 16384), (16384, 1), (1, 16385), None),
     ("u8_8192sq_dst_pitch_8195", 1, (8192, 8192), (8192, 1), (1, 8195), None),
+    # tall tiles: the shifted form from 2048 tall tiles (bf16, u8 above), a
+    # ragged one, and bf16 with aligned destination rows from 16384
+    ("bf16_8192sq_dst_pitch_8193", 2, (8192, 8192), (8192, 1), (1, 8193), None),
+    ("bf16_8000x8100_dst_pitch_8003", 2, (8000, 8100), (8100, 1), (1, 8003), None),
+    ("u8_4x2048x8192_dst_pitch_2051", 1, (4, 2048, 8192), (2048 * 8192, 8192, 1), (8192 * 2051, 1, 2051), None),
+    ("bf16_16384sq_src_pitch_16385", 2, (16384, 16384), (16385, 1), (1, 16384), None),
     ("f64_4096sq_src_pitch_4097", 8, (4096, 4096), (4097, 1), (1, 4096), None),
     ("bf16_4096sq_src_swizzle_323", 2, (4096, 4096), (4096, 1), (1, 4096), (3, 2, 3)),
 ]
