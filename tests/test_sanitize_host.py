@@ -41,8 +41,10 @@ def test_host_code_is_clean_under_asan_and_ubsan(tmp_path):
     env = dict(os.environ, TPL_LIBRARY=lib, LD_PRELOAD=sanitize_build.runtime(),
                ASAN_OPTIONS=f"detect_leaks=0:halt_on_error=1:log_path={logs}/asan",
                UBSAN_OPTIONS=f"print_stacktrace=1:halt_on_error=1:log_path={logs}/ubsan")
-    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "-m", "not gpu"]
-                         + SUITES, cwd=ROOT, env=env, capture_output=True, text=True, timeout=1200)
+    # four worker processes (each inherits the preloaded runtime and the
+    # report paths, which get the process id appended)
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "-m", "not gpu",
+                          "-n", "4"] + SUITES, cwd=ROOT, env=env, capture_output=True, text=True, timeout=1200)
     reports = "".join(f.read_text()[:3000] for f in sorted(logs.iterdir()))
     assert not reports, reports
     out = res.stdout + res.stderr
