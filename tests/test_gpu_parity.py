@@ -381,6 +381,45 @@ def test_big_index_paths(case):
     check_full(name, got, ref)
 
 
+BIG_ETILE = [
+    # name, w, extents, src strides, dst strides, src swizzle: the element
+    # tiles' 64-bit instances (tall vector form, shifted and aligned
+    # destination rows; the element form)
+    ("etile_tall_u8_dst_pitch_46403", 1, (46400, 46400), (46400, 1), (1, 46403), None),
+    ("etile_tall_bf16_src_pitch_65601", 2, (32800, 65600), (65601, 1), (1, 32800), None),
+    ("etile_element_u8_src_swizzle_203", 1, (46400, 46400), (46400, 1), (1, 46400), (2, 0, 3)),
+]
+
+
+@pytest.mark.parametrize("case", BIG_ETILE, ids=lambda c: c[0])
+def test_big_element_tiles(case):
+    """Element tiles over at least 2^31 elements: the whole result against
+    the oracle's, byte for byte, sentinel bytes kept."""
+    torch = _torch()
+    name, w, ext, ss, ds, zs = case
+    assert ext[0] * ext[1] >= 1 << 31
+    plan = tpl.tpl_plan(w, ext, ss, ds, src_swizzle=zs)
+    assert plan.kernel == "etile", plan
+    print(f"\n[case] big element tiles {name}: tile {tuple(plan.tile)}", flush=True)
+    nbs, nbd = cosize(ext, ss) * w, cosize(ext, ds) * w
+    gen = torch.Generator("cuda").manual_seed(8)
+    x = torch.randint(0, 256, (nbs,), dtype=torch.uint8, device="cuda", generator=gen)
+    d = torch.full((nbd,), SENTINEL, dtype=torch.uint8, device="cuda")
+    tpl.permute(d, x, ext, ss, ds, dtype_bytes=w, src_swizzle=zs)
+    torch.cuda.synchronize()
+    xh = x.cpu().numpy()
+    del x
+    got = d.cpu().numpy()
+    del d
+    torch.cuda.empty_cache()
+    ref = np.full(nbd, SENTINEL, dtype=np.uint8)
+    if zs is None:
+        ref = oracle_threads(xh, ref, w, ext, ss, ds, 1)
+    else:
+        oracle.permute(xh, ref, w, ext, ss, ds, (0, 0), 1, zs, None)
+    check_full(name, got, ref)
+
+
 def test_big_in_place_transpose():
     """A 65536 x 65536 byte matrix (2^32 elements) transposed in place by the
     tile-pair swap kernel's 64-bit instance, against the oracle's
