@@ -440,3 +440,18 @@ def test_etile_vector_model_in_place(w, n, pitch, batch, gap, offset):
     # whole before its stores, and items never write bytes of other items
     out, _, _ = model(x, w, (n, n), (pitch, 1), (1, pitch), (offset, offset), batch, (item, item), out=x.copy())
     assert np.array_equal(out, ref)
+
+
+@pytest.mark.parametrize("w,n,pitch,batch,gap,offset", [(1, 100, 101, 7, 0, 0), (2, 60, 61, 9, 3, 1), (1, 128, 131, 3, 5, 2)])
+def test_etile_tall_model_in_place(w, n, pitch, batch, gap, offset):
+    """The same in-place property with the tall tiles (the planner takes them
+    for such layouts from 2048 items): one tile per item, read whole before
+    its stores, the buffer ends as the oracle's permutation."""
+    item = n * pitch + gap
+    ext, ss, ds = (batch, n, n), (item, pitch, 1), (item, 1, pitch)
+    x = synth.random_bytes(14, (offset + batch * item) * w).copy()
+    ref = x.copy()
+    oracle.permute(x, ref, w, ext, ss, ds, (offset, offset), 1)
+    out, _, _ = model(x, w, (n, n), (pitch, 1), (1, pitch), (offset, offset), batch, (item, item), out=x.copy(),
+                      shape=TALL[w])
+    assert np.array_equal(out, ref)

@@ -80,10 +80,14 @@ CASES = [
     # items) before it writes any of the item
     ("u8_100_pitch101_batched_one_tile", 1, 100, 101, 7, 0, 0),
     ("u16_60_pitch61_batched_one_tile", 2, 60, 61, 9, 3, 1),
+    # the same with enough items for the tall element tiles
+    ("u8_100_pitch101_4096_items_tall", 1, 100, 101, 4096, 0, 0),
+    ("u16_60_pitch61_4096_items_tall", 2, 60, 61, 4096, 3, 1),
 ]
 
 ONE_TILE = {"u32_64_one_tile": "lds", "u8_100_pitch101_batched_one_tile": "etile",
-            "u16_60_pitch61_batched_one_tile": "etile"}
+            "u16_60_pitch61_batched_one_tile": "etile", "u8_100_pitch101_4096_items_tall": "etile",
+            "u16_60_pitch61_4096_items_tall": "etile"}
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
