@@ -139,6 +139,29 @@ def test_random_unaligned_transposes_match_oracle():
     assert sum(n for (k, w), n in kernels.items() if k == "etile" and w <= 4) >= 30 * SCALE
 
 
+def test_random_tall_element_tiles_match_oracle():
+    """Random unaligned transposes of 1- and 2-byte elements large enough for
+    the tall element tiles (unaligned destination rows, at least 2048 tall
+    tiles: 32-80 MiB each way), byte for byte against the oracle."""
+    rng = np.random.default_rng(2048)
+    done = 0
+    while done < 6 * SCALE:
+        w = int(rng.choice([1, 2]))
+        eb, ea = int(rng.integers(2000, 9000)), int(rng.integers(2000, 9000))
+        tall_tb, tall_ta = (256, 128) if w == 1 else (256, 64)
+        if -(-eb // tall_tb) * -(-ea // tall_ta) < 2048 or eb * ea * w > (80 << 20):
+            continue
+        ps = ea + int(rng.integers(0, 9))
+        pd = eb + int(rng.integers(1, 16))
+        offs = (int(rng.integers(0, 8)), int(rng.integers(0, 8)))
+        if (pd * w) % 16 == 0 and (offs[1] * w) % 16 == 0:
+            continue
+        p = tpl.tpl_plan(w, (eb, ea), (ps, 1), (1, pd), offs, 1)
+        assert p.ok and p.kernel == "etile" and tuple(p.tile) == (tall_tb, tall_ta), p
+        run_case(f"tall_{done}", w, (eb, ea), (ps, 1), (1, pd), offs, 1, seed=3000 + done)
+        done += 1
+
+
 def test_random_record_layouts_match_oracle():
     rng = np.random.default_rng(7)
     kernels = collections.Counter()
