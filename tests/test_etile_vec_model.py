@@ -384,6 +384,46 @@ def test_etile_vector_lds_is_conflict_free(w, pm):
     check_banks(w, VSHAPES[w], pm, ways)
 
 
+def shifted_phase2_ways(w, shape):
+    """Phase 2 with unaligned destination rows: column aa's destination lead
+    is (D0 + aa * dpm) mod 16 (dpm: the destination row pitch in bytes mod
+    16), so its chunk q starts at row delta / w + q * E (delta the bytes to
+    the next 16-byte boundary) and step j reads that row + j.  Returns the
+    worst and the mean number of dwords per bank over one half-wave's
+    reads, across leads."""
+    TB, TA, rp, sk, le, g = shape
+    QD, E = TB * w // 16, 16 // w
+    worst, tot, n = 1, 0, 0
+    for pm in sorted({0, 2 * w % 16, 8}):
+        for dpm in range(w, 16, w):
+            for L0 in sorted({0, (3 * w) % 16}):
+                for D0 in (0, (5 * w) % 16):
+                    for c0 in range(0, TA, max(1, 64 // QD)):
+                        for j in range(E):
+                            for first in (0, 32):
+                                addrs = []
+                                for lane in range(first, first + 32):
+                                    q, aa = lane % QD, c0 + lane // QD
+                                    lead = (D0 + aa * dpm) % 16
+                                    bb = ((16 - lead) % 16) // w + q * E + j
+                                    addrs.append(vrow(bb, rp, sk, le) + (L0 + bb * pm) % 16 + aa * w)
+                                k = ways_aligned(addrs, w, 32)
+                                worst, tot, n = max(worst, k), tot + k, n + 1
+    return worst, tot / n
+
+
+def test_etile_shifted_form_banks():
+    """Unaligned destination rows give each column of a half-wave its own
+    first row.  The tall bf16 tile reads one column per half-wave and stays
+    conflict-free; the tiles with several columns per half-wave do not
+    (rocprofv3 on MI355X: 0.01, 0.40, 0.70 and 0.45 conflict cycles per
+    active LDS cycle for tall bf16, bf16, u8 and tall u8)."""
+    assert shifted_phase2_ways(2, TALL[2]) == (1, 1.0)
+    for w, shape, mean_max in ((2, VSHAPES[2], 1.6), (1, VSHAPES[1], 2.7), (1, TALL[1], 1.7)):
+        worst, mean = shifted_phase2_ways(w, shape)
+        assert 1 < mean < mean_max, (w, shape, worst, mean)
+
+
 @pytest.mark.parametrize("w", [1, 2])
 def test_etile_tall_lds_is_conflict_free(w):
     """The tall tiles over every lead step: phase 1 on the same pass model;
