@@ -31,6 +31,7 @@ OUT_OF_PLACE = [
     ("lds_bf16_4096sq_strided", 2, (4096, 4096), (4096, 1), (1, 4096), 1, None, "lds"),
     ("etile_bf16_8192sq_pitch8196", 2, (8192, 8192), (8196, 1), (1, 8192), 1, None, "etile"),
     ("etile_swizzled_bf16_1024sq", 2, (1024, 1024), (1024, 1), (1, 1024), 1, (3, 2, 3), "etile"),
+    ("etile_tall_bf16_8192sq_dst_pitch8193", 2, (8192, 8192), (8192, 1), (1, 8193), 1, None, "etile"),
     ("rec_float3_2p20", 4, (1 << 20, 3), (3, 1), (1, 1 << 20), 1, None, "rec"),
     ("copy_runs_f32", 4, (64, 128, 1024), (131072, 1024, 1), (1024, 65536, 1), 1, None, "copy"),
     ("quad_u8_sf", 1, (4, 32), (32, 1), (1, 4), 1 << 16, None, "quad"),
