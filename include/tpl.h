@@ -111,10 +111,10 @@ typedef struct {
     int32_t k_w, shift_w, mask_w;   /* GFX950 LDS kernel: XOR of the LDS write phase */
     int32_t kernel;                 /* TPL_KERNEL_* (GFX950 only) */
     int32_t tile[2];                /* tile extents in elements along (b, a), the destination-
-                                       and the source-contiguous mode: LDS, SWAP, QUAD and REC
-                                       kernels */
+                                       and the source-contiguous mode: LDS, SWAP, QUAD, REC and
+                                       ETILE kernels (ETILE: the width's tile or its tall tile) */
     int32_t chunks_per_thread;      /* 16-byte source chunks each thread loads, LDS kernel */
-    int32_t lds_pitch;              /* LDS row pitch in bytes, LDS kernel */
+    int32_t lds_pitch;              /* LDS row pitch in bytes: LDS, SWAP and ETILE kernels */
     int64_t grid, block;            /* launch shape of the main kernel */
 } tpl_plan_info;
 
