@@ -21,9 +21,9 @@ namespace tpl {
 // registers, packs sub-dword elements into destination-order dwords and
 // stores 16 bytes.  Both XORs are the planner's smallest conflict-free k for
 // the measured gfx950 LDS banks.  Tiles of 4- to 16-byte elements store with
-// device scope (st16_dev): 4096^2 x 16 B 90.3 -> 88.0 us, the 16 MiB and
-// 32 MiB 4-D permutes 1.2 % faster; 1- and 2-byte tiles measured the same or
-// up to 2 % slower that way and keep st16.
+// device scope (st16_dev): 4096^2 x 16 B 90.3 -> 88.0 us, the 32 MiB and
+// 64 MiB 4-D permutes (4- and 8-byte elements) 1.2 % faster; 1- and 2-byte
+// tiles measured the same or up to 2 % slower that way and keep st16.
 
 template <int W, int TB, int TA, int CPT, int WW, int NB, bool BIG, bool SWZ>
 __device__ __forceinline__ void lds_loop(const LdsArgs& a, uint8_t* lds) {
