@@ -36,6 +36,11 @@ Readings where the pages are silent (each listed in the design notes):
   lets stride-1 sub-4-byte reads fail, as the "How inputs change the
   algorithm" table says).  An element of w > 4 bytes covers w/4 consecutive
   banks and the warp is served in groups of 128/w lanes.
+
+Parity unpinned: that last sentence (elements of 8 and 16 bytes).  No value on
+the pages fixes it, and the tests' brute-force simulator restates the same
+reading, so for those widths this oracle is checked against itself only.  The
+1- to 4-byte model is pinned by the pages' worked example and declines.
 """
 
 from __future__ import annotations
