@@ -174,7 +174,8 @@ int tpl_permute_swizzled(const void *src, void *dst, int dtype_bytes, int rank,
  * swizzle).  With TPL_GEOM_PAGES32 it runs the pages' method on one warp
  * region: shard, P = elements / 32, and the smallest k whose XOR swizzle
  * makes the read and the write phase bank-conflict-free (declines with
- * TPL_E_NO_K otherwise).  With TPL_GEOM_GFX950 it returns the plan
+ * TPL_E_NO_K otherwise; a region of more than 4096 elements per lane
+ * declines with TPL_E_LAYOUT, since the search simulates every step).  With TPL_GEOM_GFX950 it returns the plan
  * tpl_permute would launch (assuming 256-byte aligned base pointers), with
  * TPL_GEOM_GFX950_INPLACE the plan it would launch with src == dst.
  *

@@ -314,9 +314,15 @@ int tpl_plan_swizzled(int dtype_bytes, int rank, const int64_t* extents, const i
         static const int64_t zero[2] = {0, 0};
         const int64_t* offs = elem_offsets ? elem_offsets : zero;
         const tpl::SwzSpec zs = tpl::spec_of(src_swizzle), zd = tpl::spec_of(dst_swizzle);
+        bool neg = false;
+        if (rank >= 1 && rank <= TPL_MAX_RANK && extents)
+            for (int i = 0; i < rank; ++i) neg = neg || extents[i] < 0;
         if (rank < 1 || rank > TPL_MAX_RANK || !extents || !src_strides || !dst_strides || batch < 0) {
             p.status = TPL_E_ARG;
             p.reason = "rank must be in 1..8, arrays non-NULL, batch >= 0";
+        } else if (neg) {
+            p.status = TPL_E_ARG;
+            p.reason = "extents must be >= 0";
         } else if (geometry == TPL_GEOM_PAGES32) {
             p = tpl::plan_pages32(dtype_bytes, rank, extents, src_strides, dst_strides, batch, zs, zd);
         } else if (geometry == TPL_GEOM_GFX950_HALFWAVE) {

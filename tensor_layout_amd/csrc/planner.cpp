@@ -183,6 +183,12 @@ Plan plan_halfwave(int w, int rank, const int64_t* ext, const int64_t* ss, const
     return plan_warp32(geometry_gfx950(), w, rank, ext, ss, ds, batch, zs, zd);
 }
 
+static bool offsets_fit(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                        const int64_t* offs, int64_t batch);
+
+// Largest P (elements per lane) the warp plan accepts.
+static constexpr int64_t kWarpPlanMaxP = 4096;
+
 // A swizzle applied to an element offset.
 static int64_t swz_elem(const SwzSpec& z, int64_t m) {
     if (z.bits == 0) return m;
@@ -221,6 +227,13 @@ Plan plan_warp32(const Geometry& g, int w, int rank, const int64_t* ext, const i
         p.reason = "layouts must slice/canonicalize: batch must be >= 1";
         return p;
     }
+    static const int64_t no_offsets[2] = {0, 0};
+    int64_t n = 0;
+    if (!count_elements(rank, ext, batch, &n) || !offsets_fit(w, rank, ext, ss, ds, no_offsets, batch)) {
+        p.status = TPL_E_LAYOUT;
+        p.reason = "layouts must slice/canonicalize: offsets overflow 64-bit addressing";
+        return p;
+    }
     p.shard = make_shard(rank, ext, ss, ds, batch);
     if (!dst_injective(p.shard)) {
         p.status = TPL_E_LAYOUT;
@@ -236,6 +249,14 @@ Plan plan_warp32(const Geometry& g, int w, int rank, const int64_t* ext, const i
     }
     int64_t P = total / lanes;
     p.P = P;
+    // The search simulates all P steps of the warp for every candidate k, so
+    // its cost grows with the region; a register-staged program holds far
+    // fewer elements per lane than this bound.
+    if (P > kWarpPlanMaxP) {
+        p.status = TPL_E_LAYOUT;
+        p.reason = "the warp program stages at most 4096 elements per lane (P = elements / 32)";
+        return p;
+    }
     int kmax = 0;
     while ((2ll << kmax) <= P && kmax < 5) ++kmax;
     int64_t digits[kMaxShard];
@@ -434,9 +455,27 @@ static bool all_aligned(const Shard& sh, int skip_a, int skip_b, int w, bool src
     return true;
 }
 
+// Overflow: the largest byte offset on each side (non-negative strides,
+// extents >= 1) must stay below 2^58, so that every sum of terms fits.
+static bool offsets_fit(int w, int rank, const int64_t* ext, const int64_t* ss, const int64_t* ds,
+                        const int64_t* offs, int64_t batch) {
+    const int64_t lim = (int64_t)1 << 58;
+    for (int side = 0; side < 2; ++side) {
+        long double span = 1;
+        for (int i = 0; i < rank; ++i) span += (long double)(ext[i] - 1) * (side ? ds[i] : ss[i]);
+        const long double hi = ((long double)offs[side] + (long double)batch * span) * w;
+        if (hi > (long double)lim) return false;
+    }
+    return true;
+}
+
 bool count_elements(int rank, const int64_t* ext, int64_t batch, int64_t* out) {
     // Product of the extents and the batch; false when it exceeds 2^62
-    // (a zero extent anywhere makes the product 0 and is never an overflow).
+    // (a zero extent anywhere makes the product 0 and is never an overflow),
+    // or when an extent or the batch is negative.
+    if (batch < 0) return false;
+    for (int i = 0; i < rank; ++i)
+        if (ext[i] < 0) return false;
     bool zero = batch == 0;
     for (int i = 0; i < rank; ++i) zero = zero || ext[i] == 0;
     if (zero) {
@@ -470,6 +509,13 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
         p.reason = "unsupported dtype byte width (must be 1, 2, 4, 8 or 16)";
         return p;
     }
+    bool neg = batch < 0;
+    for (int i = 0; i < rank; ++i) neg = neg || ext[i] < 0;
+    if (neg) {
+        p.status = TPL_E_ARG;
+        p.reason = "extents and batch must be >= 0";
+        return p;
+    }
     int64_t n = 0;
     if (!count_elements(rank, ext, batch, &n)) {
         p.status = TPL_E_LAYOUT;
@@ -493,17 +539,10 @@ static Plan plan_core(int w, int rank, const int64_t* ext, const int64_t* ss, co
         p.reason = "layouts must slice/canonicalize: negative element offsets";
         return p;
     }
-    // Overflow: the largest byte offset on each side must fit comfortably.
-    const int64_t lim = (int64_t)1 << 58;
-    for (int side = 0; side < 2; ++side) {
-        long double span = 1;
-        for (int i = 0; i < rank; ++i) span += (long double)(ext[i] - 1) * (side ? ds[i] : ss[i]);
-        long double hi = ((long double)offs[side] + (long double)batch * span) * w;
-        if (hi > (long double)lim) {
-            p.status = TPL_E_LAYOUT;
-            p.reason = "layouts must slice/canonicalize: offsets overflow 64-bit addressing";
-            return p;
-        }
+    if (!offsets_fit(w, rank, ext, ss, ds, offs, batch)) {
+        p.status = TPL_E_LAYOUT;
+        p.reason = "layouts must slice/canonicalize: offsets overflow 64-bit addressing";
+        return p;
     }
     p.shard = make_shard(rank, ext, ss, ds, batch);
     const Shard& sh = p.shard;

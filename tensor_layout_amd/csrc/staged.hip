@@ -175,6 +175,11 @@ static int staged_impl(const void* src, void* dst, int w, int rank, const int64_
     if (!src || !dst) return fail_status(TPL_E_ARG, "src and dst must not be NULL");
     if (offs[0] < 0 || offs[1] < 0) return fail_status(TPL_E_LAYOUT, "layouts must slice/canonicalize: negative offsets");
 
+    // The item size rule first (the warp plan's search simulates every step).
+    int64_t item_n = 1;
+    for (int i = 0; i < rank; ++i) item_n = ext[i] > 1024 ? 1025 : std::min<int64_t>(item_n * ext[i], 1025);
+    if (item_n % 32 != 0 || item_n > 1024)
+        return fail_status(TPL_E_LAYOUT, "staged permute needs prod(extents) = 32 * P with P a power of two <= 32");
     // The per-item program: the pages' warp plan on the half-wave bank model.
     Plan p = plan_halfwave(w, rank, ext, ss, ds, 1, zs, zd);
     if (p.status != TPL_OK && p.status != TPL_E_NO_K) return fail_status(p.status, p.reason);

@@ -673,3 +673,72 @@ def test_high_bit_swizzle_never_takes_a_plain_only_kernel():
     assert tpl.tpl_plan(16, *r16).kernel == "reg16"
     for base in (25, 26, 28):
         assert tpl.tpl_plan(16, *r16, dst_swizzle=(1, base, 1)).kernel not in ("rec", "reg16")
+
+
+def test_warp_plan_bounds_its_search():
+    """The pages' warp plan simulates every step of one 32-lane program over
+    the region; regions past 4096 elements per lane decline at once
+    (TPL_E_LAYOUT) instead of simulating for hours, on both warp geometries
+    and in the staged entry's item check."""
+    import time
+    tpl.tpl_plan(4, (4, 32), (32, 1), (1, 4))   # loads the library outside the timed calls
+    for geo in (tpl.TPL_GEOM_PAGES32, tpl.TPL_GEOM_GFX950_HALFWAVE):
+        t0 = time.time()
+        p = tpl.tpl_plan(1, (8,), (64,), (8,), (1000, 1), 1 << 40, geometry=geo)
+        assert p.status == tpl.TPL_E_LAYOUT and time.time() - t0 < 1.0, (geo, p)
+        # at the bound the search still runs (4096 elements per lane)
+        p = tpl.tpl_plan(4, (4096, 32), (32, 1), (1, 4096), geometry=geo)
+        assert p.status in (tpl.TPL_OK, tpl.TPL_E_NO_K) and p.P == 4096, (geo, p)
+        p = tpl.tpl_plan(4, (4097, 32), (32, 1), (1, 4097), geometry=geo)
+        assert p.status == tpl.TPL_E_LAYOUT, (geo, p)
+    sp, dp = 1 << 20, 1 << 30   # never dereferenced: the call declines first
+    t0 = time.time()
+    st = tpl.tpl_permute_staged(sp, dp, 1, (1 << 40,), (1,), (1,), (0, 0), 1, -1)
+    assert st == tpl.TPL_E_LAYOUT and time.time() - t0 < 1.0
+
+
+def test_plan_rejects_negative_extents_and_overflow():
+    """tpl_plan validates like tpl_permute: a negative extent or batch is
+    TPL_E_ARG on every geometry; spans past 64-bit addressing are
+    TPL_E_LAYOUT on the warp geometries too."""
+    for geo in (tpl.TPL_GEOM_GFX950, tpl.TPL_GEOM_GFX950_INPLACE, tpl.TPL_GEOM_PAGES32,
+                tpl.TPL_GEOM_GFX950_HALFWAVE):
+        p = tpl.tpl_plan(4, (-128, 3, 1000), (3000, 1000, 1), (1, 128, 384), geometry=geo)
+        assert p.status == tpl.TPL_E_ARG, (geo, p)
+        p = tpl.tpl_plan(4, (4, 32), (32, 1), (1, 4), (0, 0), -1, geometry=geo)
+        assert p.status == tpl.TPL_E_ARG, (geo, p)
+    for geo in (tpl.TPL_GEOM_PAGES32, tpl.TPL_GEOM_GFX950_HALFWAVE, tpl.TPL_GEOM_GFX950):
+        p = tpl.tpl_plan(2, (7,), (1 << 62,), (1,), (0, 0), 2, geometry=geo)
+        assert p.status == tpl.TPL_E_LAYOUT, (geo, p)
+        p = tpl.tpl_plan(4, (1 << 40, 127), (16, 64), (1 << 32, 127), (0, 0), 3, geometry=geo)
+        assert p.status == tpl.TPL_E_LAYOUT, (geo, p)
+
+
+def test_plan_survives_hostile_arguments():
+    """Random hostile arguments (huge, zero and negative extents and strides,
+    odd widths, invalid swizzles and geometries) through tpl_plan: every
+    call returns a status promptly.  Under the sanitizer build (the host
+    sanitizer test reruns this file) any overflow or stray access fails."""
+    import random
+    import time
+    rng = random.Random(20261203)
+    vals = [0, 1, 2, 3, 4, 7, 8, 15, 16, 31, 32, 64, 127, 128, 1000, 4097, 1 << 20, (1 << 31) - 1, 1 << 31,
+            1 << 32, 1 << 40, 1 << 62, -1, -2, -128, -(1 << 31), -(1 << 62)]
+    geos = [tpl.TPL_GEOM_GFX950, tpl.TPL_GEOM_GFX950_INPLACE, tpl.TPL_GEOM_GFX950_HALFWAVE, tpl.TPL_GEOM_PAGES32, 99]
+    statuses = set()
+    t0 = time.time()
+    for _ in range(3000):
+        rank = rng.randint(1, 8)
+        w = rng.choice([1, 2, 3, 4, 5, 8, 16, 32, 0, -4])
+        ext = [rng.choice(vals[:16]) if rng.random() < 0.8 else rng.choice(vals) for _ in range(rank)]
+        ss = [rng.choice(vals) for _ in range(rank)]
+        ds = [rng.choice(vals) for _ in range(rank)]
+        offs = (rng.choice(vals), rng.choice(vals))
+        batch = rng.choice([0, 1, 2, 3, 1 << 20, 1 << 40, -1])
+        zs = rng.choice([None, None, (2, 2, 3), (3, 0, 3), (16, 32, 16), (1, 47, 1), (-1, 0, 0), (17, 0, 17)])
+        zd = rng.choice([None, None, (2, 2, 3), (3, 3, 4)])
+        p = tpl.tpl_plan(w, ext, ss, ds, offs, batch, geometry=rng.choice(geos), src_swizzle=zs, dst_swizzle=zd)
+        statuses.add(p.status)
+    assert time.time() - t0 < 120
+    assert statuses <= {tpl.TPL_OK, tpl.TPL_E_ARG, tpl.TPL_E_DTYPE_WIDTH, tpl.TPL_E_LAYOUT, tpl.TPL_E_NO_K,
+                        tpl.TPL_E_ALIAS}, statuses
