@@ -162,6 +162,38 @@ def test_random_tall_element_tiles_match_oracle():
         done += 1
 
 
+def test_random_degenerate_layouts_match_oracle():
+    """Source layouts the definition allows but a permutation never has:
+    zero strides (broadcast reads), strides smaller than the inner span
+    (overlapping reads), size-1 modes; the destination a one-to-one layout
+    (a permuted row-major order, sometimes padded); widths 1-16, offsets and
+    batches.  Byte for byte against the oracle."""
+    rng = np.random.default_rng(31)
+    kernels = collections.Counter()
+    done = 0
+    while done < 40 * SCALE:
+        w = int(rng.choice([1, 2, 4, 8, 16]))
+        rank = int(rng.integers(1, 7))
+        ext = [int(rng.choice([1, 2, 3, 4, 7, 8, 16, 32, 33, 64])) for _ in range(rank)]
+        n = int(np.prod(ext))
+        if n > 1 << 17:
+            continue
+        order = list(rng.permutation(rank))
+        ds, acc = [0] * rank, 1
+        for ax in reversed(order):
+            ds[ax] = acc
+            acc *= ext[ax] + int(rng.choice([0, 0, 1, 5]))
+        ss = [int(rng.choice([0, 0, 1, 2, 3, 17, 64, 1000])) for _ in range(rank)]
+        offs = (int(rng.integers(0, 9)), int(rng.integers(0, 9)))
+        batch = int(rng.choice([1, 1, 2, 3]))
+        p = tpl.tpl_plan(w, ext, ss, ds, offs, batch)
+        assert p.ok, (ext, ss, ds, p)
+        kernels[p.kernel] += 1
+        run_case(f"degenerate_{done}", w, ext, ss, ds, offs, batch, seed=4000 + done)
+        done += 1
+    print("kernel mix:", dict(kernels), flush=True)
+
+
 def test_random_record_layouts_match_oracle():
     rng = np.random.default_rng(7)
     kernels = collections.Counter()
